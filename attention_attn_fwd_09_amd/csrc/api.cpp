@@ -1,0 +1,307 @@
+// C ABI of libattn: argument checks, workspace sizing, planning and kernel dispatch.
+//
+// Every check runs on the host before the first HIP call, so a rejected call launches nothing and
+// writes nothing (the fused-attention write-up, zwxr.cn, section 2.3, on declaring format, dtype
+// and tiling metadata up front so that a mismatch fails at once instead of late).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "attn.h"
+#include "kernels.h"
+#include "params.h"
+
+using namespace attn;
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+constexpr int MAX_BLOCK_COLS = 1024;  // key tiles per layout row the forward kernel can list
+
+size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+size_t elem_size(int32_t dtype) { return dtype == ATTN_F32 ? 4 : 2; }
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+Range range_of(const void* p, size_t bytes) { return Range{(uintptr_t)p, (uintptr_t)p + bytes}; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
+
+const attn_mask kNoMask = {ATTN_MASK_NONE, nullptr, nullptr, 0, 0, 64, 64};
+
+// Checks shared by forward and backward. `mask` is never null here.
+attn_status check_problem(const attn_problem* p, const attn_mask* m, float scale) {
+  if (p->batch < 1 || p->heads_q < 1 || p->heads_kv < 1 || p->seq_q < 1 || p->seq_k < 1 || p->head_dim < 1)
+    return ATTN_ERR_SHAPE;
+  if (p->heads_q % p->heads_kv != 0) return ATTN_ERR_SHAPE;
+  if (p->dtype != ATTN_F32 && p->dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+  if (!(std::isfinite(scale) && scale >= 0.0f)) return ATTN_ERR_SHAPE;
+  switch (m->kind) {
+    case ATTN_MASK_NONE: break;
+    case ATTN_MASK_CAUSAL:
+      if (p->seq_q != p->seq_k) return ATTN_ERR_SHAPE;
+      break;
+    case ATTN_MASK_PADDING:
+      if (m->lengths == nullptr) return ATTN_ERR_MASK;
+      break;
+    case ATTN_MASK_BLOCK:
+      if (m->block_layout == nullptr) return ATTN_ERR_MASK;
+      if (m->block_q != 64 || m->block_k != 64) return ATTN_ERR_MASK;
+      if (m->layout_stride_b < 0 || m->layout_stride_h < 0) return ATTN_ERR_MASK;
+      if (ceil_div(p->seq_k, 64) > MAX_BLOCK_COLS) return ATTN_ERR_UNSUPPORTED;
+      break;
+    default: return ATTN_ERR_MASK;
+  }
+  if (p->head_dim != 64 && p->head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+  // per-(batch, head) slices are addressed with 32-bit byte offsets
+  const int64_t es = (int64_t)elem_size(p->dtype);
+  if ((int64_t)p->seq_q * p->head_dim * es >= (int64_t(1) << 31)) return ATTN_ERR_UNSUPPORTED;
+  if ((int64_t)p->seq_k * p->head_dim * es >= (int64_t(1) << 31)) return ATTN_ERR_UNSUPPORTED;
+  if ((int64_t)p->batch * p->heads_q * ceil_div(p->seq_q, 64) >= (int64_t(1) << 31)) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+int64_t layout_bytes(const attn_problem* p, const attn_mask* m) {
+  const int64_t nbq = ceil_div(p->seq_q, 64), nbk = ceil_div(p->seq_k, 64);
+  return (int64_t)(p->batch - 1) * m->layout_stride_b + (int64_t)(p->heads_q - 1) * m->layout_stride_h + nbq * nbk;
+}
+
+int fwd_tile_m(const attn_problem* p, const attn_mask* m) {
+  return p->dtype == ATTN_F32 ? fwd_f32_block_m() : fwd_bf16_block_m(p->head_dim, m->kind);
+}
+
+bool fwd_needs_plan(const attn_problem* p, const attn_mask* m) {
+  return p->dtype == ATTN_BF16 && (m->kind == ATTN_MASK_PADDING || m->kind == ATTN_MASK_BLOCK);
+}
+
+size_t fwd_ws(const attn_problem* p, const attn_mask* m) {
+  if (!fwd_needs_plan(p, m)) return 0;
+  const int64_t items = (int64_t)p->batch * p->heads_q * ceil_div(p->seq_q, fwd_tile_m(p, m));
+  return align_up((size_t)items * 4);
+}
+
+struct BwdSizes {
+  int bq, bk, n_qt, n_kt;
+  int64_t q_items, kv_items;
+  size_t delta_off, kv_off, q_off, total;
+};
+
+BwdSizes bwd_sizes(const attn_problem* p) {
+  BwdSizes s;
+  s.bq = bwd_block_q(p->head_dim);
+  s.bk = bwd_block_k(p->head_dim);
+  s.n_qt = ceil_div(p->seq_q, s.bq);
+  s.n_kt = ceil_div(p->seq_k, s.bk);
+  s.q_items = (int64_t)p->batch * p->heads_q * s.n_qt;
+  s.kv_items = (int64_t)p->batch * p->heads_kv * s.n_kt;
+  s.delta_off = 0;
+  s.kv_off = align_up((size_t)p->batch * p->heads_q * p->seq_q * 4);
+  s.q_off = s.kv_off + align_up((size_t)s.kv_items * 4);
+  s.total = s.q_off + align_up((size_t)s.q_items * 4);
+  return s;
+}
+
+attn_status hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(attn_status s) {
+  switch (s) {
+    case ATTN_OK: return "success";
+    case ATTN_ERR_NULL: return "a required pointer is NULL";
+    case ATTN_ERR_SHAPE: return "invalid sizes (dimension < 1, heads_q not a multiple of heads_kv, seq_q != seq_k for a causal mask, or scale not finite and >= 0)";
+    case ATTN_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    case ATTN_ERR_DTYPE: return "unknown dtype";
+    case ATTN_ERR_MASK: return "invalid mask descriptor (unknown kind, missing lengths or layout, block size other than 64, negative stride)";
+    case ATTN_ERR_WORKSPACE: return "workspace too small or missing";
+    case ATTN_ERR_ALIAS: return "an output overlaps an input or another output";
+    case ATTN_ERR_UNSUPPORTED: return "valid but unsupported problem (head_dim must be 64 or 128; sizes beyond the 32-bit slice limit; backward needs bf16)";
+    case ATTN_ERR_HIP: return "the HIP runtime reported an error";
+  }
+  return "unknown status";
+}
+
+int32_t attn_version(void) { return 100; }
+
+size_t attn_fwd_workspace_bytes(const attn_problem* problem, const attn_mask* mask) {
+  if (problem == nullptr) return 0;
+  const attn_mask* m = mask ? mask : &kNoMask;
+  if (check_problem(problem, m, 1.0f) != ATTN_OK) return 0;
+  return fwd_ws(problem, m);
+}
+
+attn_status attn_fwd(const attn_problem* problem, const void* Q, const void* K, const void* V,
+                     const attn_mask* mask, float scale, void* O, float* LSE, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  if (problem == nullptr || Q == nullptr || K == nullptr || V == nullptr || O == nullptr || LSE == nullptr)
+    return ATTN_ERR_NULL;
+  const attn_mask* m = mask ? mask : &kNoMask;
+  const attn_problem* p = problem;
+  attn_status st = check_problem(p, m, scale);
+  if (st != ATTN_OK) return st;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE)) return ATTN_ERR_ALIGN;
+  const size_t need = fwd_ws(p, m);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return ATTN_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return ATTN_ERR_ALIGN;
+
+  const size_t es = elem_size(p->dtype);
+  const size_t qbytes = (size_t)p->batch * p->heads_q * p->seq_q * p->head_dim * es;
+  const size_t kvbytes = (size_t)p->batch * p->heads_kv * p->seq_k * p->head_dim * es;
+  const Range rq = range_of(Q, qbytes), rk = range_of(K, kvbytes), rv = range_of(V, kvbytes);
+  const Range ro = range_of(O, qbytes), rl = range_of(LSE, (size_t)p->batch * p->heads_q * p->seq_q * 4);
+  const Range rw = range_of(workspace, need);
+  for (Range out : {ro, rl}) {
+    if (overlap(out, rq) || overlap(out, rk) || overlap(out, rv)) return ATTN_ERR_ALIAS;
+  }
+  if (overlap(ro, rl)) return ATTN_ERR_ALIAS;
+  if (need > 0) {
+    for (Range r : {rq, rk, rv, ro, rl})
+      if (overlap(rw, r)) return ATTN_ERR_ALIAS;
+  }
+  if (m->kind == ATTN_MASK_PADDING) {
+    const Range rlen = range_of(m->lengths, (size_t)p->batch * 4);
+    if (overlap(rlen, ro) || overlap(rlen, rl) || (need > 0 && overlap(rlen, rw))) return ATTN_ERR_ALIAS;
+  }
+  if (m->kind == ATTN_MASK_BLOCK) {
+    const Range rlay = range_of(m->block_layout, (size_t)layout_bytes(p, m));
+    if (overlap(rlay, ro) || overlap(rlay, rl) || (need > 0 && overlap(rlay, rw))) return ATTN_ERR_ALIAS;
+  }
+
+  // ---- launch ----
+  hipStream_t s = (hipStream_t)stream;
+  const int bm = fwd_tile_m(p, m);
+  FwdParams fp;
+  std::memset(&fp, 0, sizeof(fp));
+  fp.q = Q; fp.k = K; fp.v = V; fp.o = O; fp.lse = LSE;
+  fp.lengths = m->lengths;
+  fp.layout = m->block_layout;
+  fp.layout_stride_b = m->layout_stride_b;
+  fp.layout_stride_h = m->layout_stride_h;
+  fp.batch = p->batch; fp.heads_q = p->heads_q; fp.heads_kv = p->heads_kv;
+  fp.seq_q = p->seq_q; fp.seq_k = p->seq_k;
+  fp.group = p->heads_q / p->heads_kv;
+  fp.n_qtiles = ceil_div(p->seq_q, bm);
+  fp.n_items = p->batch * p->heads_q * fp.n_qtiles;
+  fp.nb_q = ceil_div(p->seq_q, 64);
+  fp.nb_k = ceil_div(p->seq_k, 64);
+  fp.scale = scale;
+  fp.scale_log2 = scale * 1.4426950408889634f;
+
+  if (p->dtype == ATTN_F32) return hip_status(launch_fwd_f32(fp, p->head_dim, m->kind, s));
+
+  if (need > 0) {
+    PlanParams pp;
+    std::memset(&pp, 0, sizeof(pp));
+    pp.mode = PLAN_FWD_Q; pp.mask = m->kind; pp.heads = p->heads_q; pp.group = fp.group;
+    pp.seq_q = p->seq_q; pp.seq_k = p->seq_k; pp.n_tiles = fp.n_qtiles; pp.tile = bm;
+    pp.n_items = fp.n_items; pp.nb_q = fp.nb_q; pp.nb_k = fp.nb_k;
+    pp.lengths = m->lengths; pp.layout = m->block_layout;
+    pp.layout_stride_b = m->layout_stride_b; pp.layout_stride_h = m->layout_stride_h;
+    pp.items = (uint32_t*)workspace;
+    st = hip_status(launch_plan(pp, s));
+    if (st != ATTN_OK) return st;
+    fp.items = (const uint32_t*)workspace;
+  }
+  return hip_status(launch_fwd_bf16(fp, p->head_dim, m->kind, s));
+}
+
+size_t attn_bwd_workspace_bytes(const attn_problem* problem, const attn_mask* mask) {
+  if (problem == nullptr) return 0;
+  const attn_mask* m = mask ? mask : &kNoMask;
+  if (check_problem(problem, m, 1.0f) != ATTN_OK) return 0;
+  if (problem->dtype != ATTN_BF16) return 0;
+  return bwd_sizes(problem).total;
+}
+
+attn_status attn_bwd(const attn_problem* problem, const void* Q, const void* K, const void* V, const void* O,
+                     const void* dO, const float* LSE, const attn_mask* mask, float scale, void* dQ, void* dK,
+                     void* dV, void* workspace, size_t workspace_bytes, void* stream) {
+  if (problem == nullptr || Q == nullptr || K == nullptr || V == nullptr || O == nullptr || dO == nullptr ||
+      LSE == nullptr || dQ == nullptr || dK == nullptr || dV == nullptr)
+    return ATTN_ERR_NULL;
+  const attn_mask* m = mask ? mask : &kNoMask;
+  const attn_problem* p = problem;
+  attn_status st = check_problem(p, m, scale);
+  if (st != ATTN_OK) return st;
+  if (p->dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  for (const void* ptr : {Q, K, V, O, dO, (const void*)LSE, (const void*)dQ, (const void*)dK, (const void*)dV})
+    if (!aligned16(ptr)) return ATTN_ERR_ALIGN;
+  const BwdSizes bs = bwd_sizes(p);
+  if (workspace == nullptr || workspace_bytes < bs.total) return ATTN_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
+
+  const size_t es = 2;
+  const size_t qbytes = (size_t)p->batch * p->heads_q * p->seq_q * p->head_dim * es;
+  const size_t kvbytes = (size_t)p->batch * p->heads_kv * p->seq_k * p->head_dim * es;
+  const Range ins[] = {range_of(Q, qbytes), range_of(K, kvbytes), range_of(V, kvbytes), range_of(O, qbytes),
+                       range_of(dO, qbytes), range_of(LSE, (size_t)p->batch * p->heads_q * p->seq_q * 4)};
+  const Range outs[] = {range_of(dQ, qbytes), range_of(dK, kvbytes), range_of(dV, kvbytes),
+                        range_of(workspace, bs.total)};
+  for (int i = 0; i < 4; ++i) {
+    for (const Range& r : ins)
+      if (overlap(outs[i], r)) return ATTN_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outs[j])) return ATTN_ERR_ALIAS;
+  }
+  if (m->kind == ATTN_MASK_PADDING) {
+    const Range rlen = range_of(m->lengths, (size_t)p->batch * 4);
+    for (const Range& r : outs)
+      if (overlap(rlen, r)) return ATTN_ERR_ALIAS;
+  }
+  if (m->kind == ATTN_MASK_BLOCK) {
+    const Range rlay = range_of(m->block_layout, (size_t)layout_bytes(p, m));
+    for (const Range& r : outs)
+      if (overlap(rlay, r)) return ATTN_ERR_ALIAS;
+  }
+
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  BwdParams bp;
+  std::memset(&bp, 0, sizeof(bp));
+  bp.q = Q; bp.k = K; bp.v = V; bp.o = O; bp.dout = dO; bp.lse = LSE;
+  bp.dq = dQ; bp.dk = dK; bp.dv = dV;
+  bp.delta = (float*)(ws + bs.delta_off);
+  bp.lengths = m->lengths; bp.layout = m->block_layout;
+  bp.layout_stride_b = m->layout_stride_b; bp.layout_stride_h = m->layout_stride_h;
+  bp.items_kv = (const uint32_t*)(ws + bs.kv_off);
+  bp.items_q = (const uint32_t*)(ws + bs.q_off);
+  bp.batch = p->batch; bp.heads_q = p->heads_q; bp.heads_kv = p->heads_kv;
+  bp.seq_q = p->seq_q; bp.seq_k = p->seq_k;
+  bp.group = p->heads_q / p->heads_kv;
+  bp.n_qtiles = bs.n_qt; bp.n_ktiles = bs.n_kt;
+  bp.nb_q = ceil_div(p->seq_q, 64); bp.nb_k = ceil_div(p->seq_k, 64);
+  bp.scale = scale;
+  bp.scale_log2 = scale * 1.4426950408889634f;
+
+  PlanParams pp;
+  std::memset(&pp, 0, sizeof(pp));
+  pp.mask = m->kind; pp.group = bp.group; pp.seq_q = p->seq_q; pp.seq_k = p->seq_k;
+  pp.nb_q = bp.nb_q; pp.nb_k = bp.nb_k; pp.lengths = m->lengths; pp.layout = m->block_layout;
+  pp.layout_stride_b = m->layout_stride_b; pp.layout_stride_h = m->layout_stride_h;
+  // dK/dV items: (b, kv head, key tile)
+  pp.mode = PLAN_BWD_KV; pp.heads = p->heads_kv; pp.n_tiles = bs.n_kt; pp.tile = bs.bk;
+  pp.n_items = (int32_t)bs.kv_items; pp.items = (uint32_t*)(ws + bs.kv_off);
+  st = hip_status(launch_plan(pp, s));
+  if (st != ATTN_OK) return st;
+  // dQ items: (b, query head, query tile)
+  pp.mode = PLAN_FWD_Q; pp.heads = p->heads_q; pp.n_tiles = bs.n_qt; pp.tile = bs.bq;
+  pp.n_items = (int32_t)bs.q_items; pp.items = (uint32_t*)(ws + bs.q_off);
+  st = hip_status(launch_plan(pp, s));
+  if (st != ATTN_OK) return st;
+
+  st = hip_status(launch_bwd_preprocess(bp, p->head_dim, s));
+  if (st != ATTN_OK) return st;
+  st = hip_status(launch_bwd_dkdv(bp, p->head_dim, m->kind, (int)bs.kv_items, s));
+  if (st != ATTN_OK) return st;
+  return hip_status(launch_bwd_dq(bp, p->head_dim, m->kind, (int)bs.q_items, s));
+}
+
+}  // extern "C"

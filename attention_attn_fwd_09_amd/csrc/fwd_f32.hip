@@ -1,0 +1,159 @@
+// Fused attention forward in fp32 (inputs, arithmetic and outputs all float32).
+//
+// Same method as the bf16 kernel (fused-attention write-up, zwxr.cn, sections 3.2-3.3: key/value
+// tiles streamed through on-chip memory, online softmax with a correction factor, O and LSE written
+// once), but on the vector ALU: one wave per 64-query tile, one query row per lane. The fp32
+// workloads are small (launch-latency bound), so this kernel favours plainness over throughput.
+#include "common.h"
+#include "kernels.h"
+
+namespace attn {
+
+namespace {
+
+constexpr int BM32 = 64;  // queries per workgroup (one per lane)
+constexpr int BN32 = 64;  // keys per tile
+
+template <int D>
+struct F32Lds {
+  static constexpr int QP = D + 1;  // padded Q row pitch (floats): lanes read different rows
+  static constexpr int Q_OFF = 0;
+  static constexpr int K_OFF = Q_OFF + BM32 * QP * 4;
+  static constexpr int V_OFF = K_OFF + BN32 * D * 4;
+  static constexpr int BYTES = V_OFF + BN32 * D * 4;
+};
+
+template <int D, int MASK>
+__global__ __launch_bounds__(64) void fwd_f32_kernel(FwdParams p) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  float* ql = (float*)(smem + F32Lds<D>::Q_OFF);
+  float* kl = (float*)(smem + F32Lds<D>::K_OFF);
+  float* vl = (float*)(smem + F32Lds<D>::V_OFF);
+  constexpr int QP = F32Lds<D>::QP;
+
+  const int lane = threadIdx.x;
+  const Item it = decode_item(blockIdx.x, p.heads_q, p.n_qtiles);
+  const int b = it.b, h = it.h, kvh = h / p.group;
+  const int q0 = it.t * BM32;
+  const int my_q = q0 + lane;
+  const size_t q_off = ((size_t)(b * p.heads_q + h) * p.seq_q) * D;
+  const size_t kv_off = ((size_t)(b * p.heads_kv + kvh) * p.seq_k) * D;
+  const float* qg = (const float*)p.q + q_off;
+  const float* kg = (const float*)p.k + kv_off;
+  const float* vg = (const float*)p.v + kv_off;
+
+  int kv_len = p.seq_k, q_len = p.seq_q;
+  if constexpr (MASK == MASK_PADDING) {
+    kv_len = clamp_len(p.lengths[b], p.seq_k);
+    q_len = clamp_len(p.lengths[b], p.seq_q);
+  }
+  const uint8_t* lay_row = nullptr;
+  if constexpr (MASK == MASK_BLOCK) {
+    lay_row = p.layout + b * p.layout_stride_b + h * p.layout_stride_h + (size_t)(q0 / 64) * p.nb_k;
+  }
+
+  // stage this tile's queries (rows past the end read as 0)
+  for (int e = lane; e < BM32 * D; e += 64) {
+    const int r = e / D, d = e % D;
+    ql[r * QP + d] = (q0 + r < p.seq_q) ? qg[(size_t)(q0 + r) * D + d] : 0.0f;
+  }
+
+  float acc[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) acc[d] = 0.0f;
+  float m_run = -INFINITY, l_run = 0.0f;
+  const float cs = p.scale_log2;
+
+  int n_kt = (kv_len + BN32 - 1) / BN32;
+  if constexpr (MASK == MASK_CAUSAL) n_kt = min(n_kt, (min(q0 + BM32, p.seq_q) - 1) / BN32 + 1);
+  if constexpr (MASK == MASK_PADDING) n_kt = (q0 < q_len) ? n_kt : 0;
+
+  for (int kt = 0; kt < n_kt; ++kt) {
+    if constexpr (MASK == MASK_BLOCK) {
+      if (lay_row[kt] == 0) continue;  // wave-uniform: whole 64x64 tile skipped
+    }
+    const int k0 = kt * BN32;
+    __syncthreads();
+    for (int e = lane; e < BN32 * D; e += 64) {
+      const int r = e / D;
+      const bool in = k0 + r < p.seq_k;
+      kl[e] = in ? kg[(size_t)k0 * D + e] : 0.0f;
+      vl[e] = in ? vg[(size_t)k0 * D + e] : 0.0f;
+    }
+    __syncthreads();
+
+    float s[BN32];
+    float mx = -INFINITY;
+#pragma unroll 4
+    for (int j = 0; j < BN32; ++j) {
+      float dot = 0.0f;
+#pragma unroll 16
+      for (int d = 0; d < D; ++d) dot = fmaf(ql[lane * QP + d], kl[j * D + d], dot);
+      const int key = k0 + j;
+      bool vis = key < kv_len;
+      if constexpr (MASK == MASK_CAUSAL) vis = vis && key <= my_q;
+      if constexpr (MASK == MASK_PADDING) vis = vis && my_q < q_len;
+      s[j] = vis ? dot * cs : -INFINITY;
+      mx = fmaxf(mx, s[j]);
+    }
+    // rows that have seen no visible key yet keep m = -inf, alpha = 1 and add exp2(-inf) = 0
+    const float m_new = fmaxf(m_run, mx);
+    const bool any = m_new != -INFINITY;
+    const float msub = any ? m_new : 0.0f;
+    const float alpha = any ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;  // m_run = -inf gives 0
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int d = 0; d < D; ++d) acc[d] *= alpha;
+    for (int j = 0; j < BN32; ++j) {
+      const float e = __builtin_amdgcn_exp2f(s[j] - msub);
+      l_run += e;
+#pragma unroll
+      for (int d = 0; d < D; ++d) acc[d] = fmaf(e, vl[j * D + d], acc[d]);
+    }
+  }
+
+  if (my_q < p.seq_q) {
+    const bool empty = !(l_run > 0.0f);
+    const float inv = empty ? 0.0f : 1.0f / l_run;
+    float* og = (float*)p.o + q_off + (size_t)my_q * D;
+#pragma unroll
+    for (int d = 0; d < D; ++d) og[d] = acc[d] * inv;
+    p.lse[(size_t)(b * p.heads_q + h) * p.seq_q + my_q] =
+        empty ? -INFINITY : (m_run + __builtin_amdgcn_logf(l_run)) * 0.69314718055994530942f;
+  }
+}
+
+template <int D, int MASK>
+hipError_t launch_f32_one(const FwdParams& p, hipStream_t stream) {
+  static bool attr_done = false;
+  const int lds = F32Lds<D>::BYTES;
+  if (!attr_done) {
+    hipError_t e = hipFuncSetAttribute((const void*)fwd_f32_kernel<D, MASK>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    attr_done = true;
+  }
+  hipLaunchKernelGGL((fwd_f32_kernel<D, MASK>), dim3(p.n_items), dim3(64), lds, stream, p);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_f32_mask(const FwdParams& p, int mask, hipStream_t stream) {
+  switch (mask) {
+    case MASK_NONE: return launch_f32_one<D, MASK_NONE>(p, stream);
+    case MASK_CAUSAL: return launch_f32_one<D, MASK_CAUSAL>(p, stream);
+    case MASK_PADDING: return launch_f32_one<D, MASK_PADDING>(p, stream);
+    default: return launch_f32_one<D, MASK_BLOCK>(p, stream);
+  }
+}
+
+}  // namespace
+
+int fwd_f32_block_m() { return BM32; }
+
+hipError_t launch_fwd_f32(const FwdParams& p, int head_dim, int mask, hipStream_t stream) {
+  return head_dim == 128 ? launch_f32_mask<128>(p, mask, stream) : launch_f32_mask<64>(p, mask, stream);
+}
+
+}  // namespace attn

@@ -1,0 +1,46 @@
+// Internal interface between the C ABI (api.cpp) and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+struct FwdParams;
+struct BwdParams;
+
+enum PlanMode : int { PLAN_FWD_Q = 0, PLAN_BWD_KV = 1 };
+
+// Input of the tile-list scheduler. Items are numbered (b * heads + h) * n_tiles + t.
+struct PlanParams {
+  int32_t mode;          // PlanMode
+  int32_t mask;          // mask kind
+  int32_t heads;         // heads_q for PLAN_FWD_Q, heads_kv for PLAN_BWD_KV
+  int32_t group;         // heads_q / heads_kv
+  int32_t seq_q, seq_k;
+  int32_t n_tiles;       // tiles per (b, h)
+  int32_t tile;          // rows per tile (BM for query tiles, BN for key tiles)
+  int32_t n_items;
+  int32_t nb_q, nb_k;
+  const int32_t* lengths;
+  const uint8_t* layout;
+  int64_t layout_stride_b, layout_stride_h;
+  uint32_t* items;       // output: item ids, longest first
+};
+
+hipError_t launch_plan(const PlanParams& p, hipStream_t stream);
+
+int fwd_bf16_block_m(int head_dim, int mask);
+hipError_t launch_fwd_bf16(const FwdParams& p, int head_dim, int mask, hipStream_t stream);
+
+int fwd_f32_block_m();
+hipError_t launch_fwd_f32(const FwdParams& p, int head_dim, int mask, hipStream_t stream);
+
+// Backward: tile sizes and launchers.
+int bwd_block_q(int head_dim);
+int bwd_block_k(int head_dim);
+hipError_t launch_bwd_preprocess(const BwdParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_bwd_dkdv(const BwdParams& p, int head_dim, int mask, int n_items, hipStream_t stream);
+hipError_t launch_bwd_dq(const BwdParams& p, int head_dim, int mask, int n_items, hipStream_t stream);
+
+}  // namespace attn

@@ -1,0 +1,54 @@
+// Plain parameter blocks passed by value from the C ABI to the kernels (no device code here).
+#pragma once
+
+#include <stdint.h>
+
+namespace attn {
+
+// Mask kinds, same values as the C ABI.
+enum MaskKind : int { MASK_NONE = 0, MASK_CAUSAL = 1, MASK_PADDING = 2, MASK_BLOCK = 3 };
+
+// Everything a kernel needs to know about one call, passed by value.
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const int32_t* lengths;       // PADDING
+  const uint8_t* layout;        // BLOCK
+  int64_t layout_stride_b, layout_stride_h;
+  const uint32_t* items;        // planner output (PADDING/BLOCK), else null
+  int32_t batch, heads_q, heads_kv, seq_q, seq_k;
+  int32_t group;                // heads_q / heads_kv
+  int32_t n_qtiles;             // ceil(seq_q / BM)
+  int32_t n_items;              // batch * heads_q * n_qtiles
+  int32_t nb_q, nb_k;           // BLOCK layout dims (64 x 64 tiles)
+  float scale;                  // softmax scale
+  float scale_log2;             // scale * log2(e)
+};
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;                 // workspace: rowsum(dO * O), fp32 [B, Hq, Sq]
+  const int32_t* lengths;
+  const uint8_t* layout;
+  int64_t layout_stride_b, layout_stride_h;
+  const uint32_t* items_kv;     // planner output for the dK/dV pass
+  const uint32_t* items_q;      // planner output for the dQ pass
+  int32_t batch, heads_q, heads_kv, seq_q, seq_k;
+  int32_t group;
+  int32_t n_qtiles, n_ktiles;
+  int32_t nb_q, nb_k;
+  float scale, scale_log2;
+};
+
+}  // namespace attn

@@ -1,0 +1,156 @@
+// Tile-list scheduler: orders the work items of one call longest-first.
+//
+// The report on the Xingchen-Cup sparse FlashAttention operator (smzdm.com), section 03, stresses
+// that the kept blocks of a sparse (or causal) mask are unevenly spread, so a static split leaves
+// cores idle; the fused-attention write-up (zwxr.cn), section 4.2, finds that "whoever finishes
+// first takes the next block" beats a static split. Here the items are sorted by cost, longest
+// first, and launched as one workgroup each: the hardware dispatcher hands the next item in the
+// list to whichever compute unit frees up first, which is that dynamic policy with a
+// longest-processing-time order on top. The same report's opening anecdote (147 microseconds of an
+// idle chip spent in a clumsy statistics step) warns that a slow prologue can cost more than it saves, so this is one short kernel with one workgroup:
+// a cost histogram in LDS, a scan, and a scatter.
+//
+// Items:
+//   FWD_Q / BWD_Q: (b, h_q, q-tile of BM rows), cost = number of 64-key tiles the tile visits.
+//   BWD_KV:        (b, h_kv, k-tile of BN rows), cost = number of (query head, q-tile) pairs.
+#include "common.h"
+#include "kernels.h"
+
+namespace attn {
+
+namespace {
+
+constexpr int NBUCKET = 4096;  // costs above this share the top bucket (order stays approximately LPT)
+constexpr int THREADS = 1024;
+
+__device__ int layout_row_union_count(const uint8_t* lay, int nb_k, int r0, int nrows, int nb_q) {
+  int count = 0;
+  for (int j = 0; j < nb_k; ++j) {
+    bool keep = false;
+    for (int r = 0; r < nrows; ++r) {
+      const int row = r0 + r;
+      if (row < nb_q && lay[(size_t)row * nb_k + j] != 0) keep = true;
+    }
+    count += keep ? 1 : 0;
+  }
+  return count;
+}
+
+__device__ int layout_col_union_count(const uint8_t* lay, int nb_k, int c0, int ncols, int nb_q) {
+  int count = 0;
+  for (int i = 0; i < nb_q; ++i) {
+    bool keep = false;
+    for (int cc = 0; cc < ncols; ++cc) {
+      const int col = c0 + cc;
+      if (col < nb_k && lay[(size_t)i * nb_k + col] != 0) keep = true;
+    }
+    count += keep ? 1 : 0;
+  }
+  return count;
+}
+
+__device__ int item_cost(const PlanParams& p, uint32_t item) {
+  const int t = (int)(item % (uint32_t)p.n_tiles);
+  const uint32_t bh = item / (uint32_t)p.n_tiles;
+  const int h = (int)(bh % (uint32_t)p.heads);
+  const int b = (int)(bh / (uint32_t)p.heads);
+  const int tile = p.tile;
+  if (p.mode == PLAN_BWD_KV) {
+    // key tile t of kv head h
+    if (p.mask == MASK_PADDING) {
+      const int L = clamp_len(p.lengths[b], p.seq_k);
+      const int Lq = clamp_len(p.lengths[b], p.seq_q);
+      return (t * tile < L) ? p.group * ((Lq + 63) / 64) : 0;
+    }
+    if (p.mask == MASK_BLOCK) {
+      int total = 0;
+      for (int g = 0; g < p.group; ++g) {
+        const int hq = h * p.group + g;
+        const uint8_t* lay = p.layout + b * p.layout_stride_b + hq * p.layout_stride_h;
+        total += layout_col_union_count(lay, p.nb_k, (t * tile) / 64, tile / 64, p.nb_q);
+      }
+      return total;
+    }
+    if (p.mask == MASK_CAUSAL) return p.group * ((p.seq_q - t * tile + 63) / 64);
+    return p.group * ((p.seq_q + 63) / 64);
+  }
+  // query tile t of query head h
+  if (p.mask == MASK_PADDING) {
+    const int L = clamp_len(p.lengths[b], p.seq_k);
+    const int Lq = clamp_len(p.lengths[b], p.seq_q);
+    return (t * tile < Lq) ? (L + 63) / 64 : 0;
+  }
+  if (p.mask == MASK_BLOCK) {
+    const uint8_t* lay = p.layout + b * p.layout_stride_b + h * p.layout_stride_h;
+    return layout_row_union_count(lay, p.nb_k, (t * tile) / 64, tile > 64 ? tile / 64 : 1, p.nb_q);
+  }
+  if (p.mask == MASK_CAUSAL) return min((p.seq_k + 63) / 64, (min(t * tile + tile, p.seq_q) - 1) / 64 + 1);
+  return (p.seq_k + 63) / 64;
+}
+
+// Block-wide exclusive scan of one value per thread (THREADS threads, wave64).
+__device__ int block_exclusive_scan(int v, int* wave_sums) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) wave_sums[wave] = incl;
+  __syncthreads();
+  if (wave == 0) {
+    int ws = lane < THREADS / 64 ? wave_sums[lane] : 0;
+    int wincl = ws;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(wincl, off, 64);
+      if (lane >= off) wincl += o;
+    }
+    if (lane < THREADS / 64) wave_sums[lane] = wincl - ws;
+  }
+  __syncthreads();
+  return wave_sums[wave] + incl - v;
+}
+
+__global__ __launch_bounds__(THREADS) void plan_kernel(PlanParams p) {
+  __shared__ int bucket[NBUCKET];
+  __shared__ int wave_sums[THREADS / 64];
+  for (int i = threadIdx.x; i < NBUCKET; i += THREADS) bucket[i] = 0;
+  __syncthreads();
+  // bucket r holds cost NBUCKET-1-r, so ascending r is descending cost
+  for (int i = threadIdx.x; i < p.n_items; i += THREADS) {
+    const int cost = min(item_cost(p, (uint32_t)i), NBUCKET - 1);
+    atomicAdd(&bucket[NBUCKET - 1 - cost], 1);
+  }
+  __syncthreads();
+  constexpr int PER = NBUCKET / THREADS;
+  int local[PER];
+  int sum = 0;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    local[k] = bucket[threadIdx.x * PER + k];
+    sum += local[k];
+  }
+  int off = block_exclusive_scan(sum, wave_sums);
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    bucket[threadIdx.x * PER + k] = off;
+    off += local[k];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < p.n_items; i += THREADS) {
+    const int cost = min(item_cost(p, (uint32_t)i), NBUCKET - 1);
+    const int pos = atomicAdd(&bucket[NBUCKET - 1 - cost], 1);
+    p.items[pos] = (uint32_t)i;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_plan(const PlanParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(THREADS), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace attn

@@ -1,0 +1,148 @@
+/*
+ * libattn: fused multi-head attention for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI. Every tensor argument is a plain device pointer to caller-owned
+ * memory; sizes travel in attn_problem. Nothing in these signatures depends
+ * on a framework.
+ *
+ * What the calls compute (sources, by page title and section):
+ *
+ *  - attn_fwd: "fused multi-head attention operator" write-up on the
+ *    Ascend CANN ops-nn path (zwxr.cn), section 3.1: inputs Q, K, V of
+ *    shape [batch, head, seq_len, head_dim] and an optional mask, output of
+ *    the same shape, each query's dot products with all keys times a scale,
+ *    a softmax over the keys, then the probability-weighted sum of V rows.
+ *    Section 3.2-3.3: computed tile by tile with a running maximum and sum
+ *    (online softmax), so the seq_len x seq_len score matrix is never stored.
+ *    Section 3.3: a mask entry of 0 sends the score to -infinity.
+ *  - attn_bwd: the Xingchen-Cup report on operator optimisation (smzdm.com),
+ *    section 03: the backward of (sparse) FlashAttention produces the three
+ *    gradients dQ, dK, dV, recomputing the attention probabilities tile by
+ *    tile because the forward kept only per-row statistics; skipped blocks
+ *    of a sparse mask are never visited.
+ *
+ * Conventions shared by every call:
+ *  - Layout: Q, O, dO, dQ are [batch, heads_q, seq_q, head_dim]; K, V, dK, dV
+ *    are [batch, heads_kv, seq_k, head_dim]; all contiguous, row-major, in the
+ *    problem's dtype. LSE is float32 [batch, heads_q, seq_q].
+ *  - Grouped-query attention: query head h reads key/value head
+ *    h / (heads_q / heads_kv).
+ *  - LSE is the natural logarithm of the softmax denominator of the scaled,
+ *    masked scores. A query row with no visible key gets O = 0 and
+ *    LSE = -infinity (and zero gradient rows).
+ *  - Execution: calls enqueue work on `stream` (a hipStream_t; NULL means the
+ *    default stream) and return without synchronising. Outputs are valid once
+ *    the stream reaches that point; inputs must stay unchanged until then.
+ *    No host<->device copies happen inside a call.
+ *  - Ownership: the library never allocates, frees or retains device memory.
+ *    Scratch space is the caller-provided `workspace`, sized by the matching
+ *    *_workspace_bytes query (the planner's item list lives there).
+ *  - Errors: all argument checks run on the host before any GPU call; on an
+ *    error nothing is launched and nothing is written. Device-resident mask
+ *    data cannot be checked on the host: padding lengths are clamped to
+ *    [0, seq] by the kernels. A failed launch returns ATTN_ERR_HIP.
+ *  - Thread safety: calls may be issued from several host threads; the only
+ *    state is the set of loaded kernels.
+ */
+#ifndef LIBATTN_ATTN_H
+#define LIBATTN_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = 1,        /* a required pointer is NULL */
+  ATTN_ERR_SHAPE = 2,       /* a size is < 1, heads_q % heads_kv != 0, or seq_q != seq_k where required */
+  ATTN_ERR_ALIGN = 3,       /* a tensor base pointer is not 16-byte aligned */
+  ATTN_ERR_DTYPE = 4,       /* unknown dtype */
+  ATTN_ERR_MASK = 5,        /* unknown mask kind, missing mask data, or block size != 64 */
+  ATTN_ERR_WORKSPACE = 6,   /* workspace smaller than the *_workspace_bytes query, or NULL when non-zero is needed */
+  ATTN_ERR_ALIAS = 7,       /* an output range overlaps an input range or another output */
+  ATTN_ERR_UNSUPPORTED = 8, /* valid but not implemented: head_dim other than 64/128, or an unsupported combination */
+  ATTN_ERR_HIP = 9          /* the HIP runtime reported an error when launching */
+} attn_status;
+
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
+
+typedef enum {
+  ATTN_MASK_NONE = 0,    /* every key visible */
+  ATTN_MASK_CAUSAL = 1,  /* key j hidden from query i when j > i; needs seq_q == seq_k */
+  ATTN_MASK_PADDING = 2, /* per batch element b: (i, j) visible iff i < len[b] and j < len[b] */
+  ATTN_MASK_BLOCK = 3    /* block_q x block_k tiles kept where the layout byte is non-zero */
+} attn_mask_kind;
+
+/* Sizes of one attention problem. dtype is an attn_dtype value. */
+typedef struct {
+  int32_t batch, heads_q, heads_kv, seq_q, seq_k, head_dim;
+  int32_t dtype;
+} attn_problem;
+
+/*
+ * Mask descriptor. kind is an attn_mask_kind value.
+ *  lengths      PADDING: device int32[batch], the valid length of both queries
+ *               and keys of each batch element (clamped to [0, seq]).
+ *  block_layout BLOCK: device uint8, one [nb_q][nb_k] row-major matrix per
+ *               (b, h) at element offset b*layout_stride_b + h*layout_stride_h,
+ *               nb_q = ceil(seq_q / block_q), nb_k = ceil(seq_k / block_k);
+ *               0 = skip the tile, non-zero = keep it. Strides of 0 share one
+ *               layout across batch elements and/or heads. A tile on a ragged
+ *               edge covers only the rows/columns that exist.
+ *  block_q, block_k  BLOCK: tile sizes; this build supports 64 x 64.
+ * Pointers a kind does not use are ignored and may be NULL.
+ */
+typedef struct {
+  int32_t kind;
+  const int32_t *lengths;
+  const uint8_t *block_layout;
+  int64_t layout_stride_b, layout_stride_h;
+  int32_t block_q, block_k;
+} attn_mask;
+
+/* Bytes of workspace attn_fwd needs for this problem and mask (0 if none). */
+size_t attn_fwd_workspace_bytes(const attn_problem *problem, const attn_mask *mask);
+
+/*
+ * Forward: O = softmax(scale * Q K^T + mask) V and LSE per query row.
+ * Q, K, V: inputs (see layout above). O: output in the problem dtype.
+ * LSE: float32 output [batch, heads_q, seq_q]. workspace: device scratch of
+ * at least attn_fwd_workspace_bytes() bytes (may be NULL if that is 0).
+ * Supported: dtype F32 or BF16; head_dim 64 or 128; every mask kind;
+ * heads_q a multiple of heads_kv.
+ */
+attn_status attn_fwd(const attn_problem *problem, const void *Q, const void *K, const void *V,
+                     const attn_mask *mask, float scale, void *O, float *LSE,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace attn_bwd needs (the planner lists and D = rowsum(dO * O)). */
+size_t attn_bwd_workspace_bytes(const attn_problem *problem, const attn_mask *mask);
+
+/*
+ * Backward: dQ, dK, dV of L = sum(dO * O) for the forward above, given the
+ * forward's O and LSE and the same mask and scale (the scale is needed to
+ * recompute the probabilities and to scale dQ and dK).
+ * Q, K, V, O, dO: inputs in the problem dtype; LSE: float32 from attn_fwd.
+ * dQ, dK, dV: outputs in the problem dtype. For grouped-query attention dK
+ * and dV sum over the query heads sharing a key/value head.
+ * Supported: dtype BF16; head_dim 128 or 64; every mask kind.
+ */
+attn_status attn_bwd(const attn_problem *problem, const void *Q, const void *K, const void *V,
+                     const void *O, const void *dO, const float *LSE, const attn_mask *mask,
+                     float scale, void *dQ, void *dK, void *dV, void *workspace,
+                     size_t workspace_bytes, void *stream);
+
+/* Static English description of a status code (never NULL). */
+const char *attn_status_string(attn_status status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBATTN_ATTN_H */

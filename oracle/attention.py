@@ -49,6 +49,7 @@ __all__ = [
     "mask_matrix",
     "attention_fwd",
     "attention_probs",
+    "attention_rows",
     "attention_bwd",
 ]
 
@@ -147,6 +148,32 @@ def attention_fwd(q, k, v, mask: MaskSpec, scale: float):
             p, l, _ = attention_probs(q, k, mask, scale, b, h)
             o[b, h] = p @ v[b, _kv_head(h, hq, hkv)]
             lse[b, h] = l
+    return o, lse
+
+
+def attention_rows(q, k, v, mask: MaskSpec, scale: float, b: int, h: int, rows):
+    """O and LSE of selected query rows of one (b, h) pair: the same definition as
+    attention_fwd, evaluated only for ``rows`` (used to sample very long sequences)."""
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    rows = np.asarray(rows)
+    hq, hkv = q.shape[1], k.shape[1]
+    g = _kv_head(h, hq, hkv)
+    sq, sk = q.shape[2], k.shape[2]
+    keep = mask_matrix(mask, b, h, sq, sk)[rows]
+    qr = np.asarray(q[b, h, rows], dtype=np.float64)
+    kg = np.asarray(k[b, g], dtype=np.float64)
+    vg = np.asarray(v[b, g], dtype=np.float64)
+    s = np.where(keep, scale * (qr @ kg.T), -np.inf)
+    nonempty = keep.any(axis=1)
+    m = np.where(nonempty, s.max(axis=1, initial=-np.inf), 0.0)
+    e = np.where(keep, np.exp(s - m[:, None]), 0.0)
+    denom = e.sum(axis=1)
+    safe = np.where(nonempty, denom, 1.0)
+    o = np.where(nonempty[:, None], (e / safe[:, None]) @ vg, 0.0)
+    with np.errstate(divide="ignore"):
+        lse = np.where(nonempty, m + np.log(safe), -np.inf)
     return o, lse
 
 

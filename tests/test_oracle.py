@@ -62,3 +62,25 @@ def test_planted_mistake_is_caught(name):
         except Exception as e:  # noqa: BLE001 - any failure counts as caught
             failures.append((check.__name__, type(e).__name__))
     assert failures, f"no pin caught the planted mistake {name}"
+
+
+def test_row_subset_matches_full_oracle():
+    """attention_rows evaluates the same definition on a subset of rows."""
+    import numpy as np
+
+    r = np.random.default_rng(3)
+    q, k, v = r.standard_normal((2, 4, 70, 8)), r.standard_normal((2, 2, 70, 8)), r.standard_normal((2, 2, 70, 8))
+    lay = (r.random((2, 2)) < 0.5).astype(np.uint8)
+    specs = [oracle.MaskSpec("none"), oracle.MaskSpec("causal"),
+             oracle.MaskSpec("padding", lengths=np.array([30, 70], np.int32)),
+             oracle.MaskSpec("block", layout=lay)]
+    rows = np.array([0, 5, 31, 63, 64, 69])
+    for spec in specs:
+        o, lse = oracle.attention_fwd(q, k, v, spec, 0.3)
+        for b in range(2):
+            for h in range(4):
+                o_r, lse_r = oracle.attention_rows(q, k, v, spec, 0.3, b, h, rows)
+                np.testing.assert_allclose(o_r, o[b, h, rows], rtol=0, atol=1e-14)
+                np.testing.assert_array_equal(np.isneginf(lse_r), np.isneginf(lse[b, h, rows]))
+                fin = np.isfinite(lse_r)
+                np.testing.assert_allclose(lse_r[fin], lse[b, h, rows][fin], rtol=0, atol=1e-14)
