@@ -92,10 +92,10 @@ struct BwdSizes {
   size_t delta_off, kv_off, q_off, total;
 };
 
-BwdSizes bwd_sizes(const attn_problem* p) {
+BwdSizes bwd_sizes(const attn_problem* p, const attn_mask* m) {
   BwdSizes s;
-  s.bq = bwd_block_q(p->head_dim);
-  s.bk = bwd_block_k(p->head_dim);
+  s.bq = bwd_block_q(p->head_dim, m->kind);
+  s.bk = bwd_block_k(p->head_dim, m->kind);
   s.n_qt = ceil_div(p->seq_q, s.bq);
   s.n_kt = ceil_div(p->seq_k, s.bk);
   s.q_items = (int64_t)p->batch * p->heads_q * s.n_qt;
@@ -108,6 +108,32 @@ BwdSizes bwd_sizes(const attn_problem* p) {
 }
 
 attn_status hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
+
+// Optional per-class event brackets (attn_set_timing_events).
+struct TimingSlot {
+  void* const* start = nullptr;
+  void* const* stop = nullptr;
+  int32_t capacity = 0;
+  int32_t* count = nullptr;
+};
+TimingSlot g_timing[ATTN_KERNEL_CLASSES];
+
+// Runs `launch` bracketed by the class's events when a hook is set.
+template <typename F>
+hipError_t timed(int cls, hipStream_t s, F&& launch) {
+  TimingSlot& t = g_timing[cls];
+  const bool on = t.capacity > 0 && t.count != nullptr && *t.count < t.capacity;
+  if (on) {
+    hipError_t e = hipEventRecord((hipEvent_t)t.start[*t.count], s);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = launch();
+  if (on && e == hipSuccess) {
+    e = hipEventRecord((hipEvent_t)t.stop[*t.count], s);
+    ++*t.count;
+  }
+  return e;
+}
 
 }  // namespace
 
@@ -130,6 +156,22 @@ const char* attn_status_string(attn_status s) {
 }
 
 int32_t attn_version(void) { return 100; }
+
+attn_status attn_set_timing_events(int32_t kernel_class, void* const* start_events, void* const* stop_events,
+                                   int32_t capacity, int32_t* count) {
+  if (kernel_class < 0 || kernel_class >= ATTN_KERNEL_CLASSES) return ATTN_ERR_SHAPE;
+  TimingSlot& t = g_timing[kernel_class];
+  if (capacity <= 0 || start_events == nullptr || stop_events == nullptr) {
+    t = TimingSlot{};
+    return ATTN_OK;
+  }
+  if (count == nullptr) return ATTN_ERR_NULL;
+  t.start = start_events;
+  t.stop = stop_events;
+  t.capacity = capacity;
+  t.count = count;
+  return ATTN_OK;
+}
 
 size_t attn_fwd_workspace_bytes(const attn_problem* problem, const attn_mask* mask) {
   if (problem == nullptr) return 0;
@@ -195,7 +237,8 @@ attn_status attn_fwd(const attn_problem* problem, const void* Q, const void* K, 
   fp.scale = scale;
   fp.scale_log2 = scale * 1.4426950408889634f;
 
-  if (p->dtype == ATTN_F32) return hip_status(launch_fwd_f32(fp, p->head_dim, m->kind, s));
+  if (p->dtype == ATTN_F32)
+    return hip_status(timed(ATTN_KERNEL_FWD, s, [&] { return launch_fwd_f32(fp, p->head_dim, m->kind, s); }));
 
   if (need > 0) {
     PlanParams pp;
@@ -206,11 +249,11 @@ attn_status attn_fwd(const attn_problem* problem, const void* Q, const void* K, 
     pp.lengths = m->lengths; pp.layout = m->block_layout;
     pp.layout_stride_b = m->layout_stride_b; pp.layout_stride_h = m->layout_stride_h;
     pp.items = (uint32_t*)workspace;
-    st = hip_status(launch_plan(pp, s));
+    st = hip_status(timed(ATTN_KERNEL_PLAN, s, [&] { return launch_plan(pp, s); }));
     if (st != ATTN_OK) return st;
     fp.items = (const uint32_t*)workspace;
   }
-  return hip_status(launch_fwd_bf16(fp, p->head_dim, m->kind, s));
+  return hip_status(timed(ATTN_KERNEL_FWD, s, [&] { return launch_fwd_bf16(fp, p->head_dim, m->kind, s); }));
 }
 
 size_t attn_bwd_workspace_bytes(const attn_problem* problem, const attn_mask* mask) {
@@ -218,7 +261,7 @@ size_t attn_bwd_workspace_bytes(const attn_problem* problem, const attn_mask* ma
   const attn_mask* m = mask ? mask : &kNoMask;
   if (check_problem(problem, m, 1.0f) != ATTN_OK) return 0;
   if (problem->dtype != ATTN_BF16) return 0;
-  return bwd_sizes(problem).total;
+  return bwd_sizes(problem, m).total;
 }
 
 attn_status attn_bwd(const attn_problem* problem, const void* Q, const void* K, const void* V, const void* O,
@@ -232,9 +275,14 @@ attn_status attn_bwd(const attn_problem* problem, const void* Q, const void* K, 
   attn_status st = check_problem(p, m, scale);
   if (st != ATTN_OK) return st;
   if (p->dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (m->kind == ATTN_MASK_BLOCK) {
+    // the dK/dV pass lists (query head, layout row) pairs of its column: 6 + 10 bits each
+    const int64_t nbq = ceil_div(p->seq_q, 64), group = p->heads_q / p->heads_kv;
+    if (nbq > 1024 || group > 63 || group * nbq > bwd_max_steps()) return ATTN_ERR_UNSUPPORTED;
+  }
   for (const void* ptr : {Q, K, V, O, dO, (const void*)LSE, (const void*)dQ, (const void*)dK, (const void*)dV})
     if (!aligned16(ptr)) return ATTN_ERR_ALIGN;
-  const BwdSizes bs = bwd_sizes(p);
+  const BwdSizes bs = bwd_sizes(p, m);
   if (workspace == nullptr || workspace_bytes < bs.total) return ATTN_ERR_WORKSPACE;
   if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
 
@@ -289,19 +337,21 @@ attn_status attn_bwd(const attn_problem* problem, const void* Q, const void* K, 
   // dK/dV items: (b, kv head, key tile)
   pp.mode = PLAN_BWD_KV; pp.heads = p->heads_kv; pp.n_tiles = bs.n_kt; pp.tile = bs.bk;
   pp.n_items = (int32_t)bs.kv_items; pp.items = (uint32_t*)(ws + bs.kv_off);
-  st = hip_status(launch_plan(pp, s));
+  st = hip_status(timed(ATTN_KERNEL_PLAN, s, [&] { return launch_plan(pp, s); }));
   if (st != ATTN_OK) return st;
   // dQ items: (b, query head, query tile)
   pp.mode = PLAN_FWD_Q; pp.heads = p->heads_q; pp.n_tiles = bs.n_qt; pp.tile = bs.bq;
   pp.n_items = (int32_t)bs.q_items; pp.items = (uint32_t*)(ws + bs.q_off);
-  st = hip_status(launch_plan(pp, s));
+  st = hip_status(timed(ATTN_KERNEL_PLAN, s, [&] { return launch_plan(pp, s); }));
   if (st != ATTN_OK) return st;
 
-  st = hip_status(launch_bwd_preprocess(bp, p->head_dim, s));
+  st = hip_status(timed(ATTN_KERNEL_BWD_PRE, s, [&] { return launch_bwd_preprocess(bp, p->head_dim, s); }));
   if (st != ATTN_OK) return st;
-  st = hip_status(launch_bwd_dkdv(bp, p->head_dim, m->kind, (int)bs.kv_items, s));
+  st = hip_status(timed(ATTN_KERNEL_BWD_DKDV, s,
+                        [&] { return launch_bwd_dkdv(bp, p->head_dim, m->kind, (int)bs.kv_items, s); }));
   if (st != ATTN_OK) return st;
-  return hip_status(launch_bwd_dq(bp, p->head_dim, m->kind, (int)bs.q_items, s));
+  return hip_status(
+      timed(ATTN_KERNEL_BWD_DQ, s, [&] { return launch_bwd_dq(bp, p->head_dim, m->kind, (int)bs.q_items, s); }));
 }
 
 }  // extern "C"

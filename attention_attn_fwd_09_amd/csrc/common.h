@@ -33,20 +33,68 @@ __device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t r, void* 
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// --- LDS swizzles of 16-byte chunks within a key row ---
-// LDS serves 256 bytes per clock from 64 four-byte banks, so a 16-byte chunk's bank group is its
-// byte offset / 16 modulo 16. K tiles are read with ds_read_b128 by 16 lanes at a time from 16
-// different rows (keys {0-3,16-19,4-7,20-23} or {8-15,24-31} of a 32-key block, same logical
-// chunk): swz_k gives those rows 16 distinct bank groups. V tiles are read with the transposing
-// ds_read_b64_tr_b16, 32 lanes at a time from 4 consecutive rows x 4 consecutive chunks: swz_v
-// gives those 16 (row, chunk) pairs distinct bank groups. Writes fill one row's chunks per 16
-// lanes, which any per-row XOR permutes without conflict.
-template <int D> __device__ __forceinline__ int swz_k(int row);
-template <> __device__ __forceinline__ int swz_k<128>(int row) { return (row & 7) | ((row >> 1) & 8); }
-template <> __device__ __forceinline__ int swz_k<64>(int row) { return ((row >> 1) & 3) | ((row >> 2) & 4); }
-template <int D> __device__ __forceinline__ int swz_v(int row);
-template <> __device__ __forceinline__ int swz_v<128>(int row) { return (row & 3) << 2; }
-template <> __device__ __forceinline__ int swz_v<64>(int row) { return ((row >> 1) & 1) << 2; }
+// --- LDS tiles: 64 rows x D bf16, rows of D*2 bytes, 16-byte chunks XOR-swizzled per row ---
+// LDS serves 256 bytes per clock from 64 four-byte banks; a 16-byte chunk's bank group is
+// (byte offset / 16) mod 16. Tiles are read in two patterns:
+//  * row fragments (ds_read_b128): 16 lanes read the same logical chunk of 16 different rows,
+//    rows {0-3,16-19,4-7,20-23} or {8-11,24-27,12-15,28-31} (+32) of the sigma32 permutation;
+//  * transposed fragments (ds_read_b64_tr_b16): 32 lanes read 4 consecutive rows (aligned to 4)
+//    times 4 consecutive chunks.
+// swz<D>(row) gives both patterns 16 distinct bank groups: its bits 2-3 (D=128) or bit 2 (D=64,
+// where two rows share one 256-byte bank span) follow the row's position inside its group of 4,
+// and its low bits separate the four 4-row groups of a row-fragment read. Writes fill one row's
+// chunks per 16 lanes, which any per-row XOR permutes without conflict.
+template <int D> __device__ __forceinline__ int swz(int row);
+template <> __device__ __forceinline__ int swz<128>(int row) {
+  return ((row & 3) << 2) | ((row >> 2) & 1) | ((row >> 3) & 2);
+}
+template <> __device__ __forceinline__ int swz<64>(int row) {
+  return (((row >> 1) & 1) << 2) | ((row >> 2) & 1) | ((row >> 3) & 2);
+}
+
+// Copy rows [row0, row0 + 64) of a [rows][D] bf16 tensor (buffer descriptor r) into an LDS tile.
+// All NW*64 threads of the workgroup take part; rows past the end of the buffer read as 0.
+template <int D, int NW>
+__device__ __forceinline__ void issue_rows(char* lds_tile, __amdgpu_buffer_rsrc_t r, int row0, int wave, int lane) {
+  constexpr int CPR = D / 8;                       // 16-byte chunks per row
+  constexpr int ROUNDS = (64 * CPR) / (NW * 64);
+#pragma unroll
+  for (int it = 0; it < ROUNDS; ++it) {
+    const int blk = it * NW + wave;                // 64-chunk (1 KiB) block written by this wave
+    const int pos = blk * 64 + lane;               // physical chunk index in the tile
+    const int row = pos / CPR;
+    const int pc = pos % CPR;
+    buffer_to_lds16(r, lds_tile + blk * 1024, (uint32_t)(row0 + row) * (D * 2) + (uint32_t)((pc ^ swz<D>(row)) * 16));
+  }
+}
+
+// Row fragment: 8 bf16 of logical chunk `chunk` of tile row `row`.
+template <int D>
+__device__ __forceinline__ bf16x8 lds_row_frag(const char* tile, int row, int chunk) {
+  return *(const bf16x8*)(tile + row * (D * 2) + ((chunk ^ swz<D>(row)) * 16));
+}
+
+// Transposed fragment: an MFMA operand whose lane holds 8 consecutive tile rows at one column.
+// row0 is the first of those 8 rows for the calling lane's half-wave, dbase the column of the
+// first lane of its 16-lane group, i16 = lane & 15; the lane receives column dbase + i16 of rows
+// row0 .. row0+7. ds_read_b64_tr_b16 works on 16-lane groups: the 4 rows of one read are each
+// assembled from 4 lanes' 8-byte pieces (lanes 4r..4r+3 supply row r) and lane i16 receives
+// element i16 of every row, so lane i16 addresses row row0 + i16/4, columns dbase + 4*(i16%4)..+3.
+template <int D>
+__device__ __forceinline__ bf16x8 lds_tr_frag(const char* tile, int row0, int dbase, int i16) {
+  const int r0 = row0 + (i16 >> 2);
+  const int r1 = r0 + 4;
+  const int d = dbase + 4 * (i16 & 3);
+  const char* p0 = tile + r0 * (D * 2) + (((d >> 3) ^ swz<D>(r0)) * 16) + (d & 7) * 2;
+  const char* p1 = tile + r1 * (D * 2) + (((d >> 3) ^ swz<D>(r1)) * 16) + (d & 7) * 2;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, p0));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, p1));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
 
 // Row permutation of a 32-key block inside the score MFMA: MFMA row r reads key sigma(r), so that
 // in the 32x32 output each half-wave holds 16 consecutive keys of its query column.

@@ -38,26 +38,6 @@ struct FwdLds {
   static constexpr int BYTES = LIST_OFF + MAX_LIST * 4 + 16;
 };
 
-// Issue the copies of key/value tile `kt` into LDS stage `st`. All NW*64 threads take part.
-template <int D, int NW>
-__device__ __forceinline__ void issue_tile(char* lds_stage, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
-                                           int kt, int wave, int lane) {
-  constexpr int CHUNKS_PER_ROW = D / 8;                       // 16-byte chunks
-  constexpr int ROUNDS = (BN * CHUNKS_PER_ROW) / (NW * 64);   // per tensor
-  char* kl = lds_stage;
-  char* vl = lds_stage + FwdLds<D>::TILE_BYTES;
-#pragma unroll
-  for (int r = 0; r < ROUNDS; ++r) {
-    const int blk = r * NW + wave;                            // 64-chunk block written by this wave
-    const int pos = blk * 64 + lane;                          // physical chunk in the tile
-    const int row = pos / CHUNKS_PER_ROW;
-    const int pc = pos % CHUNKS_PER_ROW;
-    const uint32_t grow = (uint32_t)(kt * BN + row) * (D * 2);
-    buffer_to_lds16(rk, kl + blk * 1024, grow + (uint32_t)((pc ^ swz_k<D>(row)) * 16));
-    buffer_to_lds16(rv, vl + blk * 1024, grow + (uint32_t)((pc ^ swz_v<D>(row)) * 16));
-  }
-}
-
 template <int D, int NW, int MASK>
 __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
   constexpr int BM = NW * 32;
@@ -152,13 +132,17 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
     return j;
   };
 
-  if (n_tiles > 0) issue_tile<D, NW>(smem, rk, rv, tile_index(0), wave, lane);
+  auto issue_tile = [&](char* stage, int kt) {
+    issue_rows<D, NW>(stage, rk, kt * BN, wave, lane);
+    issue_rows<D, NW>(stage + FwdLds<D>::TILE_BYTES, rv, kt * BN, wave, lane);
+  };
+  if (n_tiles > 0) issue_tile(smem, tile_index(0));
 
   for (int j = 0; j < n_tiles; ++j) {
     wait_vmem();
     __syncthreads();  // tile j is in LDS; every wave is done with the stage tile j+1 will overwrite
     if (j + 1 < n_tiles)
-      issue_tile<D, NW>(smem + ((j + 1) & 1) * FwdLds<D>::STAGE_BYTES, rk, rv, tile_index(j + 1), wave, lane);
+      issue_tile(smem + ((j + 1) & 1) * FwdLds<D>::STAGE_BYTES, tile_index(j + 1));
 
     const int kt = tile_index(j);
     const int k0 = kt * BN;
@@ -183,12 +167,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int row = kb * 32 + sigma32(c);
-        const int chunk = (2 * ks + hh) ^ swz_k<D>(row);
-        const bf16x8 a = *(const bf16x8*)(kl + row * (D * 2) + chunk * 16);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
-      }
+      for (int kb = 0; kb < 2; ++kb)
+        s[kb] = mfma32(lds_row_frag<D>(kl, kb * 32 + sigma32(c), 2 * ks + hh), qf[ks], s[kb]);
     }
 
     // ---- online softmax on this lane's 32 scores (keys k0 + kb*32 + hh*16 + i) ----
@@ -235,23 +215,13 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
     }
 
     // ---- O^T += V^T P^T; chunk kc holds keys kb*32 + hh*16 + hc*8 + 0..7 for lane half hh ----
-    const int g = lane >> 4, i16 = lane & 15;
-    const int dsub = (g & 1) * 16;
+    const int dsub = ((lane >> 4) & 1) * 16, i16 = lane & 15;
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
-      const int kb = kc >> 1, hc = kc & 1;
+      const int row0 = (kc >> 1) * 32 + hh * 16 + (kc & 1) * 8;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int d = db * 32 + dsub + 4 * (i16 & 3);
-        const int row0 = kb * 32 + hh * 16 + hc * 8 + (i16 >> 2);
-        const int row1 = row0 + 4;
-        const char* a0p = vl + row0 * (D * 2) + (((d >> 3) ^ swz_v<D>(row0)) * 16) + (d & 7) * 2;
-        const char* a1p = vl + row1 * (D * 2) + (((d >> 3) ^ swz_v<D>(row1)) * 16) + (d & 7) * 2;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, a0p));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, a1p));
-        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kc], acc[db], 0, 0, 0);
-      }
+      for (int db = 0; db < DB; ++db)
+        acc[db] = mfma32(lds_tr_frag<D>(vl, row0, db * 32 + dsub, i16), pb[kc], acc[db]);
     }
   }
 

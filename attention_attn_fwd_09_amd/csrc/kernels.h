@@ -37,8 +37,9 @@ int fwd_f32_block_m();
 hipError_t launch_fwd_f32(const FwdParams& p, int head_dim, int mask, hipStream_t stream);
 
 // Backward: tile sizes and launchers.
-int bwd_block_q(int head_dim);
-int bwd_block_k(int head_dim);
+int bwd_block_q(int head_dim, int mask);
+int bwd_block_k(int head_dim, int mask);
+int bwd_max_steps();  // (query head, query tile) pairs one dK/dV workgroup can list for a block mask
 hipError_t launch_bwd_preprocess(const BwdParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdParams& p, int head_dim, int mask, int n_items, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdParams& p, int head_dim, int mask, int n_items, hipStream_t stream);

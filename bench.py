@@ -1,0 +1,302 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention hot path on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input: the fused forward
+(O, LSE) and the backward (dQ, dK, dV) of the block-sparse workload (batch 2, 16 heads, seq 4096,
+head_dim 128, 64x64 blocks kept with p = 0.25 plus the diagonal), the only measured workload that
+exercises every step of the path. Inputs are resident in HBM before the timed region starts.
+
+Prints one JSON line. `value` is algorithmic TFLOP/s: 4*D flops per visible (query, key) pair for
+the forward plus 10*D for the backward (five products); masked and skipped work is not counted.
+`roofline` describes the dominant kernel, timed live with HIP events on the library's stream;
+`cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--all]
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+METRIC = "attention fwd/bwd TFLOP/s (bf16) + % of MFMA peak on 1 MI355X, seq 2048-8192"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+KERNEL_NAMES = {0: "plan", 1: "fwd", 2: "bwd_pre", 3: "bwd_dkdv", 4: "bwd_dq"}
+
+
+def log(msg: str):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """Timing events from the HIP runtime itself (they are recorded by the library on its stream)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n: int):
+        arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            ev = ctypes.c_void_p()
+            rc = self.hip.hipEventCreate(ctypes.byref(ev))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed: {rc}")
+            arr[i] = ev
+        return arr
+
+    def elapsed_ms(self, a, b) -> float:
+        self.hip.hipEventSynchronize(b)
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return ms.value
+
+    def destroy(self, arr):
+        for ev in arr:
+            self.hip.hipEventDestroy(ev)
+
+
+def visible_pairs(w, inp) -> int:
+    """Number of (query, key) pairs the mask keeps, summed over batch and query heads."""
+    import torch
+    b, hq, sq, sk = w.batch, w.heads_q, w.seq_q, w.seq_k
+    if w.mask == "none":
+        return b * hq * sq * sk
+    if w.mask == "causal":
+        return b * hq * sq * (sq + 1) // 2
+    if w.mask == "padding":
+        return hq * int(sum(int(n) ** 2 for n in inp["lengths"].tolist()))
+    lay = inp["layout"].to(torch.int64)
+    rows = torch.clamp(sq - torch.arange(lay.shape[-2]) * w.block, max=w.block)
+    cols = torch.clamp(sk - torch.arange(lay.shape[-1]) * w.block, max=w.block)
+    per = (lay * rows[:, None] * cols[None, :]).sum()
+    return int(per) * (1 if lay.dim() == 4 else b * hq)
+
+
+def run_gpu(args):
+    import torch
+
+    from attention_attn_fwd_09_amd import binding as lib
+    from attention_attn_fwd_09_amd.inputs import WORKLOADS, workload_inputs
+
+    cfg = 5
+    w = WORKLOADS[cfg]
+    dev = torch.device("cuda:0")
+    inp = workload_inputs(cfg, with_do=True)
+    q, k, v, do = (inp[x].to(dev).contiguous() for x in ("q", "k", "v", "do"))
+    layout = inp["layout"].to(dev).contiguous()
+    mask = lib.Mask(kind="block", layout=layout)
+    scale = inp["scale"]
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws_f = torch.empty(max(1, lib.attn_fwd_workspace_bytes(q, k, mask)), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(max(1, lib.attn_bwd_workspace_bytes(q, k, mask)), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        lib.attn_fwd(q, k, v, mask=mask, scale=scale, out=o, lse=lse, workspace=ws_f, stream=stream)
+        lib.attn_bwd(q, k, v, o, do, lse, mask=mask, scale=scale, dq=dq, dk=dk, dv=dv, workspace=ws_b,
+                     stream=stream)
+
+    pairs = visible_pairs(w, inp)
+    d = w.head_dim
+    flops_fwd = 4 * d * pairs
+    flops_bwd = 10 * d * pairs
+    flops_step = flops_fwd + flops_bwd
+    # flops each kernel class executes per launch (its own products, recomputation included)
+    kernel_flops = {1: 4 * d * pairs, 3: 8 * d * pairs, 4: 6 * d * pairs}
+    kernel_bytes = {2: w.batch * w.heads_q * w.seq_q * (2 * d * 2 + 4)}
+
+    hip = HipEvents()
+    clib = lib.load_library()
+    clib.attn_set_timing_events.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                            ctypes.POINTER(ctypes.c_int32)]
+    clib.attn_set_timing_events.restype = ctypes.c_int
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # which kernel dominates: bracket every class for a few untimed steps
+    probe_steps = 3
+    cap = 4 * probe_steps
+    probes = {}
+    for cls in KERNEL_NAMES:
+        st, sp = hip.create(cap), hip.create(cap)
+        cnt = ctypes.c_int32(0)
+        clib.attn_set_timing_events(cls, st, sp, cap, ctypes.byref(cnt))
+        probes[cls] = (st, sp, cnt)
+    for _ in range(probe_steps):
+        step()
+    torch.cuda.synchronize()
+    per_class = {}
+    for cls, (st, sp, cnt) in probes.items():
+        clib.attn_set_timing_events(cls, None, None, 0, None)
+        n = cnt.value
+        per_class[cls] = (sum(hip.elapsed_ms(st[i], sp[i]) for i in range(n)) / probe_steps, n // probe_steps)
+        hip.destroy(st)
+        hip.destroy(sp)
+    dominant = max(per_class, key=lambda c: per_class[c][0])
+    log("per-step kernel time (ms): " + ", ".join(f"{KERNEL_NAMES[c]}={per_class[c][0]:.4f}x{per_class[c][1]}"
+                                                  for c in per_class))
+
+    # timed region: the dominant kernel is bracketed on the library's stream
+    st, sp = hip.create(args.steps), hip.create(args.steps)
+    cnt = ctypes.c_int32(0)
+    clib.attn_set_timing_events(dominant, st, sp, args.steps, ctypes.byref(cnt))
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    clib.attn_set_timing_events(dominant, None, None, 0, None)
+    ms_total = t0.elapsed_time(t1)
+    ms_step = ms_total / args.steps
+    n_dom = cnt.value
+    dom_ms = sum(hip.elapsed_ms(st[i], sp[i]) for i in range(n_dom)) / max(n_dom, 1)
+    hip.destroy(st)
+    hip.destroy(sp)
+
+    tflops = flops_step / (ms_step * 1e-3) / 1e12
+    if dominant in kernel_flops:
+        achieved = kernel_flops[dominant] / (dom_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    else:
+        achieved = kernel_bytes.get(dominant, 0) / (dom_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+    roofline["kernel"] = KERNEL_NAMES[dominant]
+    roofline["kernel_ms"] = round(dom_ms, 5)
+
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "batch": w.batch, "heads": w.heads_q, "seq_len": w.seq_q, "head_dim": d,
+            "mask": "block 64x64, p=0.25 + diagonal (shared by all heads)",
+            "step": "attn_fwd + attn_bwd",
+            "visible_pairs": pairs,
+            "flops_per_step": flops_step,
+            "fwd_tflops_share": round(flops_fwd / flops_step, 4),
+        },
+        "pct_of_bf16_mfma_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "wall_s_timed": round(wall, 4),
+        "roofline": roofline,
+        "kernels_ms_per_step": {KERNEL_NAMES[c]: round(per_class[c][0], 5) for c in per_class},
+    }
+    sample = None
+    if not args.no_cpu_baseline:
+        sample = cpu_baseline(w, inp, pairs)
+    result["cpu_baseline"] = sample
+
+    if args.all:
+        forward_all(lib, torch, dev, WORKLOADS, workload_inputs)
+    return result
+
+
+def cpu_baseline(w, inp, pairs_total):
+    """fp64 oracle (as it stands) on a bounded sample: forward + backward of a few (b, h) pairs."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # noqa: BLE001
+        cores = len(os.sched_getaffinity(0))
+    q64, k64, v64, do64 = (inp[x].to(dtype=__import__("torch").float64).numpy() for x in ("q", "k", "v", "do"))
+    spec = oracle.MaskSpec(kind="block", layout=inp["layout"].numpy(), block_q=w.block, block_k=w.block)
+    heads_done = 0
+    t0 = time.perf_counter()
+    budget = 12.0
+    total_heads = w.batch * w.heads_q
+    while heads_done < total_heads:
+        b, h = divmod(heads_done, w.heads_q)
+        qs, ks, vs, dos = (x[b:b + 1, h:h + 1] for x in (q64, k64, v64, do64))
+        sub = oracle.MaskSpec(kind="block", layout=spec.layout, block_q=w.block, block_k=w.block)
+        oracle.attention_fwd(qs, ks, vs, sub, inp["scale"])
+        oracle.attention_bwd(qs, ks, vs, dos, sub, inp["scale"])
+        heads_done += 1
+        if time.perf_counter() - t0 > budget:
+            break
+    secs = time.perf_counter() - t0
+    flops = 14 * w.head_dim * pairs_total * heads_done / total_heads
+    return {"value": round(flops / secs / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"fwd+bwd of {heads_done} of {total_heads} (batch, head) pairs of the same workload, "
+                      f"{secs:.1f} s; value counts the same algorithmic flops per pair as the GPU line",
+            "seconds": round(secs, 2)}
+
+
+def forward_all(lib, torch, dev, workloads, workload_inputs):
+    """Extra diagnostics on stderr: forward-only TFLOP/s of every measured workload."""
+    for cfg, w in workloads.items():
+        inp = workload_inputs(cfg)
+        q, k, v = (inp[x].to(dev).contiguous() for x in ("q", "k", "v"))
+        m = lib.Mask(kind=w.mask, lengths=None if inp["lengths"] is None else inp["lengths"].to(dev),
+                     layout=None if inp["layout"] is None else inp["layout"].to(dev))
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        ws = torch.empty(max(1, lib.attn_fwd_workspace_bytes(q, k, m)), dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            lib.attn_fwd(q, k, v, mask=m, scale=inp["scale"], out=o, lse=lse, workspace=ws)
+        torch.cuda.synchronize()
+        n = 20
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            lib.attn_fwd(q, k, v, mask=m, scale=inp["scale"], out=o, lse=lse, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / n
+        fl = 4 * w.head_dim * visible_pairs(w, inp)
+        log(json.dumps({"workload": w.name, "fwd_ms": round(ms, 5), "fwd_tflops": round(fl / ms / 1e9, 2),
+                        "pct_peak": round(100 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2)}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--all", action="store_true", help="also print forward timings of every workload to stderr")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the attention path here is built and "
+              "timed on a single MI355X and has no multi-GPU mode.", file=sys.stderr)
+        sys.exit(2)
+    res = run_gpu(args)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

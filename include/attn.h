@@ -135,6 +135,27 @@ attn_status attn_bwd(const attn_problem *problem, const void *Q, const void *K, 
                      float scale, void *dQ, void *dK, void *dV, void *workspace,
                      size_t workspace_bytes, void *stream);
 
+/*
+ * Kernel timing hook, for profiling tools. Kernel classes: */
+typedef enum {
+  ATTN_KERNEL_PLAN = 0,     /* tile-list scheduler */
+  ATTN_KERNEL_FWD = 1,      /* fused forward */
+  ATTN_KERNEL_BWD_PRE = 2,  /* backward preprocess, Delta = rowsum(dO * O) */
+  ATTN_KERNEL_BWD_DKDV = 3, /* backward dK/dV pass */
+  ATTN_KERNEL_BWD_DQ = 4,   /* backward dQ pass */
+  ATTN_KERNEL_CLASSES = 5
+} attn_kernel_class;
+/*
+ * While set for a class, each launch of that class records start_events[i] before it and
+ * stop_events[i] after it (hipEventRecord on the call's stream), i = *count, then increments
+ * *count; launches beyond `capacity` are not bracketed. The events (hipEvent_t, created by the
+ * caller with timing enabled) and `count` are caller-owned and must outlive the setting. Pass
+ * capacity 0 (or NULL arrays) to clear. Not thread-safe: set it while no other thread calls the
+ * library. Returns ATTN_ERR_SHAPE for an unknown class, ATTN_ERR_NULL for a missing count.
+ */
+attn_status attn_set_timing_events(int32_t kernel_class, void *const *start_events, void *const *stop_events,
+                                   int32_t capacity, int32_t *count);
+
 /* Static English description of a status code (never NULL). */
 const char *attn_status_string(attn_status status);
 

@@ -51,6 +51,7 @@ __all__ = [
     "attention_probs",
     "attention_rows",
     "attention_bwd",
+    "attention_bwd_head",
 ]
 
 
@@ -209,3 +210,23 @@ def attention_bwd(q, k, v, do, mask: MaskSpec, scale: float):
             dq[b, h] = scale * (ds @ k[b, g])
             dk[b, g] += scale * (ds.T @ q[b, h])
     return dq, dk, dv
+
+
+def attention_bwd_head(q, k, v, do, mask: MaskSpec, scale: float, b: int, h: int):
+    """The contribution of one (b, h) pair to the gradients: dQ[b, h] and the parts of dK[b, g],
+    dV[b, g] that query head h adds (g = h // G); the same chain rule as attention_bwd,
+    evaluated for one pair only (used to sample long sequences)."""
+    hq, hkv = np.asarray(q).shape[1], np.asarray(k).shape[1]
+    g = _kv_head(h, hq, hkv)
+    q64 = np.asarray(q[b:b + 1, h:h + 1], dtype=np.float64)
+    k64 = np.asarray(k[b:b + 1, g:g + 1], dtype=np.float64)
+    v64 = np.asarray(v[b:b + 1, g:g + 1], dtype=np.float64)
+    do64 = np.asarray(do[b:b + 1, h:h + 1], dtype=np.float64)
+    sub = MaskSpec(kind=mask.kind, block_q=mask.block_q, block_k=mask.block_k)
+    if mask.kind == "padding":
+        sub.lengths = np.asarray(mask.lengths)[b:b + 1]
+    if mask.kind == "block":
+        lay = np.asarray(mask.layout)
+        sub.layout = lay[b:b + 1, h:h + 1] if lay.ndim == 4 else lay
+    dq, dk, dv = attention_bwd(q64, k64, v64, do64, sub, scale)
+    return dq[0, 0], dk[0, 0], dv[0, 0]

@@ -1,0 +1,117 @@
+"""GPU parity of the backward pass (dQ, dK, dV) against the fp64 oracle, through the C ABI.
+
+The GPU backward consumes the GPU forward's O and LSE, as a caller would. Tolerance per gradient:
+max|g - g_ref| / max|g_ref| <= 5e-2 on the same bf16-rounded inputs.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from attention_attn_fwd_09_amd.inputs import WORKLOADS, Workload, make_inputs, workload_inputs
+from tests.gpu_helpers import TOL_BF16_BWD_REL, device_inputs, lib_mask, libattn, oracle_mask, say, to_np64
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_fwd_bwd(w: Workload, inp: dict):
+    d = device_inputs(inp)
+    m = lib_mask(w, d)
+    o, lse = libattn.attn_fwd(d["q"], d["k"], d["v"], mask=m, scale=inp["scale"])
+    dq, dk, dv = libattn.attn_bwd(d["q"], d["k"], d["v"], o, d["do"], lse, mask=m, scale=inp["scale"])
+    torch.cuda.synchronize()
+    return o, lse, dq, dk, dv
+
+
+def _rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    denom = float(np.max(np.abs(ref)))
+    num = float(np.max(np.abs(got - ref)))
+    if denom == 0.0:
+        return num
+    return num / denom
+
+
+def _check_grads(grads_gpu, grads_ref, label):
+    for name, got, ref in zip(("dq", "dk", "dv"), grads_gpu, grads_ref):
+        assert np.all(np.isfinite(got)), f"{label} {name}: non-finite"
+        e = _rel_err(got, ref)
+        say(f"  {label} {name}: rel max err {e:.3e}")
+        assert e <= TOL_BF16_BWD_REL, f"{label} {name}: rel max err {e} > {TOL_BF16_BWD_REL}"
+
+
+SMALL = []
+for d in (64, 128):
+    for mask in ("none", "causal", "padding", "block"):
+        for (b, hq, hkv, s) in ((1, 2, 2, 1), (2, 2, 1, 17), (1, 4, 2, 130), (2, 2, 2, 257), (1, 2, 2, 520)):
+            if mask == "padding" and s < 4:
+                continue
+            SMALL.append((d, mask, b, hq, hkv, s))
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "-".join(map(str, c)))
+def test_bwd_small_parity(gpu_available, case):
+    d, mask, b, hq, hkv, s = case
+    w = Workload(f"bwd_{case}", "bf16", b, hq, hkv, s, s, d, mask, backward=True,
+                 len_range=(max(1, s // 4), s), keep_prob=0.3)
+    seed = 31 + s * 3 + d
+    say(f"bwd small {case} seed {seed}")
+    inp = make_inputs(w, seed)
+    _, _, dq, dk, dv = _gpu_fwd_bwd(w, inp)
+    ref = oracle.attention_bwd(to_np64(inp["q"]), to_np64(inp["k"]), to_np64(inp["v"]), to_np64(inp["do"]),
+                               oracle_mask(w, inp), inp["scale"])
+    _check_grads((to_np64(dq), to_np64(dk), to_np64(dv)), ref, str(case))
+
+
+def test_bwd_block_per_head_layout_gqa(gpu_available):
+    w = Workload("bwd_blk_ph", "bf16", 2, 4, 2, 300, 300, 128, "block", backward=True, keep_prob=0.3,
+                 layout_per_head=True)
+    inp = make_inputs(w, 77)
+    _, _, dq, dk, dv = _gpu_fwd_bwd(w, inp)
+    ref = oracle.attention_bwd(to_np64(inp["q"]), to_np64(inp["k"]), to_np64(inp["v"]), to_np64(inp["do"]),
+                               oracle_mask(w, inp), inp["scale"])
+    _check_grads((to_np64(dq), to_np64(dk), to_np64(dv)), ref, "block per-head gqa")
+
+
+def test_bwd_empty_rows_give_zero_gradients(gpu_available):
+    w = Workload("bwd_pad0", "bf16", 3, 2, 2, 150, 150, 64, "padding", backward=True)
+    inp = make_inputs(w, 4)
+    inp["lengths"] = torch.tensor([0, 1, 100], dtype=torch.int32)
+    _, _, dq, dk, dv = _gpu_fwd_bwd(w, inp)
+    assert torch.all(dq[0] == 0) and torch.all(dk[0] == 0) and torch.all(dv[0] == 0)
+    assert torch.all(dq[2, :, 100:] == 0) and torch.all(dk[2, :, 100:] == 0) and torch.all(dv[2, :, 100:] == 0)
+    ref = oracle.attention_bwd(to_np64(inp["q"]), to_np64(inp["k"]), to_np64(inp["v"]), to_np64(inp["do"]),
+                               oracle_mask(w, inp), inp["scale"])
+    _check_grads((to_np64(dq), to_np64(dk), to_np64(dv)), ref, "padding 0/1/100")
+
+
+def test_bwd_deterministic(gpu_available):
+    w = Workload("bwd_det", "bf16", 1, 4, 2, 600, 600, 128, "block", backward=True, keep_prob=0.3)
+    inp = make_inputs(w, 5)
+    r1 = _gpu_fwd_bwd(w, inp)
+    r2 = _gpu_fwd_bwd(w, inp)
+    for a, b in zip(r1, r2):
+        assert torch.equal(a, b)
+
+
+def test_bwd_workload_block_sparse_full_size(gpu_available):
+    """The block-sparse forward+backward workload at full size: sampled heads against the oracle,
+    and the exact identities sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i on every head."""
+    config = 5
+    w = WORKLOADS[config]
+    say(f"bwd workload {config} {w.name}")
+    inp = workload_inputs(config)
+    _, _, dq, dk, dv = _gpu_fwd_bwd(w, inp)
+    spec = oracle_mask(w, inp)
+    q64, k64, v64, do64 = (to_np64(inp[x]) for x in ("q", "k", "v", "do"))
+    for (b, h) in ((0, 0), (1, 15), (1, 6)):
+        ref = oracle.attention_bwd_head(q64, k64, v64, do64, spec, inp["scale"], b, h)
+        _check_grads((to_np64(dq[b, h]), to_np64(dk[b, h]), to_np64(dv[b, h])), ref, f"cfg5 b{b} h{h}")
+    # identities on every (b, h): the rows of dS sum to zero, and every row of P sums to one
+    dk_sum = dk.float().sum(dim=2)
+    dv_sum = dv.float().sum(dim=2)
+    do_sum = inp["do"].float().sum(dim=2).to(dv.device)
+    scale_k = dk.float().abs().sum(dim=2).clamp_min(1.0)
+    scale_v = dv.float().abs().sum(dim=2).clamp_min(1.0)
+    assert float((dk_sum.abs() / scale_k).max()) < 2e-2
+    assert float(((dv_sum - do_sum).abs() / scale_v).max()) < 2e-2

@@ -84,3 +84,25 @@ def test_row_subset_matches_full_oracle():
                 np.testing.assert_array_equal(np.isneginf(lse_r), np.isneginf(lse[b, h, rows]))
                 fin = np.isfinite(lse_r)
                 np.testing.assert_allclose(lse_r[fin], lse[b, h, rows][fin], rtol=0, atol=1e-14)
+
+
+def test_bwd_head_matches_full_oracle():
+    """attention_bwd_head is the per-(b, h) share of attention_bwd."""
+    import numpy as np
+
+    r = np.random.default_rng(4)
+    q, k, v = r.standard_normal((2, 4, 40, 8)), r.standard_normal((2, 2, 40, 8)), r.standard_normal((2, 2, 40, 8))
+    do = r.standard_normal(q.shape)
+    lay4 = (r.random((2, 4, 1, 1)) < 2).astype(np.uint8)
+    for spec in (oracle.MaskSpec("causal"), oracle.MaskSpec("padding", lengths=np.array([13, 40], np.int32)),
+                 oracle.MaskSpec("block", layout=lay4)):
+        dq, dk, dv = oracle.attention_bwd(q, k, v, do, spec, 0.5)
+        dk_sum, dv_sum = np.zeros_like(dk), np.zeros_like(dv)
+        for b in range(2):
+            for h in range(4):
+                dq_h, dk_h, dv_h = oracle.attention_bwd_head(q, k, v, do, spec, 0.5, b, h)
+                np.testing.assert_allclose(dq_h, dq[b, h], rtol=0, atol=1e-13)
+                dk_sum[b, h // 2] += dk_h
+                dv_sum[b, h // 2] += dv_h
+        np.testing.assert_allclose(dk_sum, dk, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(dv_sum, dv, rtol=0, atol=1e-13)
