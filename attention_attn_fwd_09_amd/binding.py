@@ -15,7 +15,7 @@ from typing import Optional
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+_LIB_PATH = os.environ.get("ATTN_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
 
 # status codes (attn_status)
 ATTN_OK = 0
@@ -60,7 +60,10 @@ _lib = None
 
 
 def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
-    """Load libattn.so once and declare the C signatures. Raises if the library is missing."""
+    """Load libattn.so once and declare the C signatures. Raises if the library is missing.
+
+    The default is the in-tree build next to this file; the ATTN_LIBRARY environment variable
+    names another build of the same library (used to compare kernel variants)."""
     global _lib
     if _lib is not None:
         return _lib

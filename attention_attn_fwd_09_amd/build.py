@@ -38,21 +38,26 @@ def _compile(src: str, extra: list[str]) -> str:
     return obj
 
 
-def build(extra_flags: list[str] | None = None, jobs: int | None = None) -> str:
-    """Compile every source and link libattn.so; returns the library path."""
+def build(extra_flags: list[str] | None = None, jobs: int | None = None, out: str | None = None,
+          build_dir: str | None = None) -> str:
+    """Compile every source and link libattn.so (or `out`); returns the library path."""
+    global BUILD
     extra = list(extra_flags or [])
+    if build_dir:
+        BUILD = build_dir
     os.makedirs(BUILD, exist_ok=True)
     srcs = _sources()
     jobs = jobs or min(len(srcs), 8)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(lambda s: _compile(s, extra), srcs))
-    tmp = LIB + ".tmp"
+    lib = out or LIB
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

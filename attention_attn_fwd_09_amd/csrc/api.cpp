@@ -235,7 +235,9 @@ attn_status attn_fwd(const attn_problem* problem, const void* Q, const void* K, 
   fp.nb_q = ceil_div(p->seq_q, 64);
   fp.nb_k = ceil_div(p->seq_k, 64);
   fp.scale = scale;
-  fp.scale_log2 = scale * 1.4426950408889634f;
+  // kernels rely on scale*log2(e) > 0 (masked scores are -inf); scale 0 runs as 1e-30, which
+  // changes no score by more than 1e-29 relative
+  fp.scale_log2 = (scale > 0.0f ? scale : 1e-30f) * 1.4426950408889634f;
 
   if (p->dtype == ATTN_F32)
     return hip_status(timed(ATTN_KERNEL_FWD, s, [&] { return launch_fwd_f32(fp, p->head_dim, m->kind, s); }));
@@ -327,7 +329,7 @@ attn_status attn_bwd(const attn_problem* problem, const void* Q, const void* K, 
   bp.n_qtiles = bs.n_qt; bp.n_ktiles = bs.n_kt;
   bp.nb_q = ceil_div(p->seq_q, 64); bp.nb_k = ceil_div(p->seq_k, 64);
   bp.scale = scale;
-  bp.scale_log2 = scale * 1.4426950408889634f;
+  bp.scale_log2 = (scale > 0.0f ? scale : 1e-30f) * 1.4426950408889634f;
 
   PlanParams pp;
   std::memset(&pp, 0, sizeof(pp));

@@ -68,6 +68,30 @@ __device__ __forceinline__ void issue_rows(char* lds_tile, __amdgpu_buffer_rsrc_
   }
 }
 
+// Register-staged variant of issue_rows: each thread loads its chunks of the 64-row tile into
+// VGPRs (load_rows) and later writes them to LDS (store_rows) at the same swizzled positions.
+template <int D, int NW>
+struct RowStage {
+  static constexpr int N = (64 * (D / 8)) / (NW * 64);
+  i32x4 v[N];
+};
+template <int D, int NW>
+__device__ __forceinline__ void load_rows(RowStage<D, NW>& st, __amdgpu_buffer_rsrc_t r, int row0, int tid) {
+  constexpr int CPR = D / 8;
+#pragma unroll
+  for (int it = 0; it < RowStage<D, NW>::N; ++it) {
+    const int pos = it * (NW * 64) + tid;
+    const int row = pos / CPR, pc = pos % CPR;
+    st.v[it] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
+        r, (uint32_t)(row0 + row) * (D * 2) + (uint32_t)((pc ^ swz<D>(row)) * 16), 0, 0));
+  }
+}
+template <int D, int NW>
+__device__ __forceinline__ void store_rows(char* lds_tile, const RowStage<D, NW>& st, int tid) {
+#pragma unroll
+  for (int it = 0; it < RowStage<D, NW>::N; ++it) *(i32x4*)(lds_tile + (it * (NW * 64) + tid) * 16) = st.v[it];
+}
+
 // Row fragment: 8 bf16 of logical chunk `chunk` of tile row `row`.
 template <int D>
 __device__ __forceinline__ bf16x8 lds_row_frag(const char* tile, int row, int chunk) {

@@ -19,6 +19,8 @@
 //    V^T operand comes from LDS through the transposing ds_read_b64_tr_b16.
 //  * the running maximum is re-based only when it grows by more than 2^8 (exact: numerator and
 //    denominator always share the same reference), which skips most accumulator rescales.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -32,22 +34,31 @@ constexpr float RESCALE_SLACK = 8.0f;  // log2 headroom before the reference max
 template <int D>
 struct FwdLds {
   static constexpr int TILE_BYTES = BN * D * 2;              // one K or V tile
-  static constexpr int STAGE_BYTES = 2 * TILE_BYTES;         // K + V
-  static constexpr int LIST_OFF = 2 * STAGE_BYTES;           // block list after two stages
   static constexpr int MAX_LIST = 1024;                      // kept key tiles per query tile
-  static constexpr int BYTES = LIST_OFF + MAX_LIST * 4 + 16;
 };
 
-template <int D, int NW, int MASK>
-__global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
+// MINW: waves per SIMD the register allocation must allow (2 lets two workgroups share a CU).
+template <int D, int NW, int MASK, int MINW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW))) void fwd_bf16_kernel(FwdParams p) {
   constexpr int BM = NW * 32;
   constexpr int KS = D / 16;   // k-steps of the score product
   constexpr int DB = D / 32;   // 32-row blocks of O^T
-  extern __shared__ __attribute__((aligned(16))) char smem[];
+  constexpr int RB = D * 2;    // bytes per tile row
+  using L = FwdLds<D>;
+  // Four separately named tiles (K and V of stage 0 and 1): the compiler can then prove that the
+  // buffer-to-LDS copy into one stage does not alias the reads of the other, and issues no
+  // vmcnt wait before those reads.
+  __shared__ __attribute__((aligned(16))) char k_st0[L::TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char v_st0[L::TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char k_st1[L::TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char v_st1[L::TILE_BYTES];
+  __shared__ uint32_t list[MASK == MASK_BLOCK ? L::MAX_LIST + 1 : 1];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 31, hh = lane >> 5;
+  const int i16 = lane & 15, dsub = ((lane >> 4) & 1) * 16;
 
   // ---- which tile of which (batch, head) ----
   Item it;
@@ -63,21 +74,18 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
 
   const size_t q_off = ((size_t)(b * p.heads_q + h) * p.seq_q) * D;
   const size_t kv_off = ((size_t)(b * p.heads_kv + kvh) * p.seq_k) * D;
-  const bf16* qg = (const bf16*)p.q + q_off;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qg, (uint32_t)p.seq_q * D * 2);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const bf16*)p.k + kv_off, (uint32_t)p.seq_k * D * 2);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const bf16*)p.v + kv_off, (uint32_t)p.seq_k * D * 2);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const bf16*)p.q + q_off, (uint32_t)p.seq_q * RB);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const bf16*)p.k + kv_off, (uint32_t)p.seq_k * RB);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const bf16*)p.v + kv_off, (uint32_t)p.seq_k * RB);
 
   // ---- key range of this item ----
   int kv_len = p.seq_k;   // keys at or beyond kv_len are masked
   int q_len = p.seq_q;    // queries at or beyond q_len see nothing
   int n_tiles;
-  uint32_t* list = (uint32_t*)(smem + FwdLds<D>::LIST_OFF);
   if constexpr (MASK == MASK_PADDING) {
-    const int L = clamp_len(p.lengths[b], p.seq_k);
-    kv_len = L;
+    kv_len = clamp_len(p.lengths[b], p.seq_k);
     q_len = clamp_len(p.lengths[b], p.seq_q);
-    n_tiles = (q0 < q_len) ? (L + BN - 1) / BN : 0;
+    n_tiles = (q0 < q_len) ? (kv_len + BN - 1) / BN : 0;
   } else if constexpr (MASK == MASK_CAUSAL) {
     const int last_q = min(q0 + BM, p.seq_q) - 1;
     n_tiles = min((p.seq_k + BN - 1) / BN, last_q / BN + 1);
@@ -103,10 +111,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
         if (bits != 0) list[count + before] = (uint32_t)j | (bits << 16);
         count += __popcll(ball);
       }
-      if (lane == 0) list[FwdLds<D>::MAX_LIST] = (uint32_t)count;
+      if (lane == 0) list[L::MAX_LIST] = (uint32_t)count;
     }
     __syncthreads();
-    n_tiles = (int)list[FwdLds<D>::MAX_LIST];
+    n_tiles = (int)list[L::MAX_LIST];
   } else {
     n_tiles = (p.seq_k + BN - 1) / BN;
   }
@@ -116,8 +124,29 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     const i32x4 raw = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
-        rq, (uint32_t)my_q * (D * 2) + (uint32_t)(ks * 32 + hh * 16), 0, 0));
+        rq, (uint32_t)my_q * RB + (uint32_t)(ks * 32 + hh * 16), 0, 0));
     qf[ks] = __builtin_bit_cast(bf16x8, raw);
+  }
+
+  // ---- per-lane LDS byte offsets inside a tile; everything else in an address is a constant ----
+  // K row fragment for k-step ks of key block kb: koff[ks] + kb * 32 rows.
+  int koff[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int row = sigma32(c);
+    koff[ks] = row * RB + (((2 * ks + hh) ^ swz<D>(row)) * 16);
+  }
+  // transposed V fragment for column block db, rows +0..3 (half 0) or +4..7 (half 1) of the
+  // 8-key chunk: voff[db][half] + (chunk base row) rows.
+  int voff[DB][2];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int row = hh * 16 + half * 4 + (i16 >> 2);
+      const int d = db * 32 + dsub + 4 * (i16 & 3);
+      voff[db][half] = row * RB + (((d >> 3) ^ swz<D>(row)) * 16) + (d & 7) * 2;
+    }
   }
 
   f32x16 acc[DB];
@@ -127,74 +156,72 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
   float l_run = 0.0f;        // this lane's partial denominator (its 16 keys of each 32-key block)
   const float cs = p.scale_log2;
 
-  auto tile_index = [&](int j) -> int {
+  auto tile_index = [&](int j) __attribute__((always_inline)) -> int {
     if constexpr (MASK == MASK_BLOCK) return (int)(list[j] & 0xffffu);
     return j;
   };
-
-  auto issue_tile = [&](char* stage, int kt) {
-    issue_rows<D, NW>(stage, rk, kt * BN, wave, lane);
-    issue_rows<D, NW>(stage + FwdLds<D>::TILE_BYTES, rv, kt * BN, wave, lane);
+  auto issue_tile = [&](auto stage_tag, int kt) __attribute__((always_inline)) {
+    constexpr int ST = decltype(stage_tag)::value;
+    issue_rows<D, NW>(ST == 0 ? k_st0 : k_st1, rk, kt * BN, wave, lane);
+    issue_rows<D, NW>(ST == 0 ? v_st0 : v_st1, rv, kt * BN, wave, lane);
   };
-  if (n_tiles > 0) issue_tile(smem, tile_index(0));
 
-  for (int j = 0; j < n_tiles; ++j) {
-    wait_vmem();
-    __syncthreads();  // tile j is in LDS; every wave is done with the stage tile j+1 will overwrite
-    if (j + 1 < n_tiles)
-      issue_tile(smem + ((j + 1) & 1) * FwdLds<D>::STAGE_BYTES, tile_index(j + 1));
-
-    const int kt = tile_index(j);
-    const int k0 = kt * BN;
-    // wave-uniform: does this wave see any key of the tile, and does it need per-element masking?
-    bool active = true, need_mask = (k0 + BN > kv_len);
-    if constexpr (MASK == MASK_CAUSAL) {
-      active = k0 <= qw0 + 31;
-      need_mask = need_mask || (k0 + BN - 1 > qw0);
-    } else if constexpr (MASK == MASK_PADDING) {
-      active = qw0 < q_len;
-      need_mask = need_mask || (qw0 + 31 >= q_len);
-    } else if constexpr (MASK == MASK_BLOCK) {
-      active = ((list[j] >> 16) >> ((wave * 32) / 64)) & 1u;
-    }
-    if (!active) continue;
-
-    const char* kl = smem + (j & 1) * FwdLds<D>::STAGE_BYTES;
-    const char* vl = kl + FwdLds<D>::TILE_BYTES;
+  // One 64-key tile for this wave's 32 queries, read from LDS stage ST. The instruction order is
+  // pinned with sched_group_barrier (masks: 0x008 MFMA, 0x100 LDS read, 0x002 VALU) so that LDS
+  // reads run two k-steps ahead of the MFMAs that consume them, and the first V fragments are in
+  // flight while the softmax runs on the vector ALU.
+  auto tile = [&](auto stage_tag, auto masked_tag, int k0) __attribute__((always_inline)) {
+    constexpr int ST = decltype(stage_tag)::value;
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const char* kl = ST == 0 ? k_st0 : k_st1;
+    const char* vl = ST == 0 ? v_st0 : v_st1;
 
     // ---- S^T = K Q^T for two 32-key blocks ----
-    f32x16 s[2] = {f32x16{}, f32x16{}};
+    f32x16 s0 = f32x16{}, s1 = f32x16{};
+    bf16x8 ka[KS], kb1[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
+      ka[ks] = *(const bf16x8*)(kl + koff[ks]);
+      kb1[ks] = *(const bf16x8*)(kl + koff[ks] + 32 * RB);
+    }
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        s[kb] = mfma32(lds_row_frag<D>(kl, kb * 32 + sigma32(c), 2 * ks + hh), qf[ks], s[kb]);
+    for (int ks = 0; ks < KS; ++ks) {
+      s0 = mfma32(ka[ks], qf[ks], s0);
+      s1 = mfma32(kb1[ks], qf[ks], s1);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int ks = 0; ks < KS - 2; ++ks) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+
+    // ---- mask (boundary tiles only): hidden scores become -inf ----
+    if constexpr (MASKED) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key0 = k0 + hh * 16 + i, key1 = key0 + 32;
+        bool v0 = key0 < kv_len, v1 = key1 < kv_len;
+        if constexpr (MASK == MASK_CAUSAL) {
+          v0 = v0 && key0 <= my_q;
+          v1 = v1 && key1 <= my_q;
+        }
+        if constexpr (MASK == MASK_PADDING) {
+          v0 = v0 && my_q < q_len;
+          v1 = v1 && my_q < q_len;
+        }
+        s0[i] = v0 ? s0[i] : -INFINITY;
+        s1[i] = v1 ? s1[i] : -INFINITY;
+      }
     }
 
     // ---- online softmax on this lane's 32 scores (keys k0 + kb*32 + hh*16 + i) ----
     float mx = -INFINITY;
-    if (need_mask) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = k0 + kb * 32 + hh * 16 + i;
-          bool vis = key < kv_len;
-          if constexpr (MASK == MASK_CAUSAL) vis = vis && key <= my_q;
-          if constexpr (MASK == MASK_PADDING) vis = vis && my_q < q_len;
-          const float t = vis ? s[kb][i] * cs : -INFINITY;
-          s[kb][i] = t;
-          mx = fmaxf(mx, t);
-        }
-      mx = partner_max(mx);
-    } else {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-      mx = partner_max(mx) * cs;
-    }
-    if (__ballot(mx > m_run + RESCALE_SLACK) != 0) {
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
+    mx = partner_max(mx) * cs;   // cs > 0, so max(s) * cs = max(s * cs); -inf stays -inf
+    if (__builtin_expect(__ballot(mx > m_run + RESCALE_SLACK) != 0, 0)) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_run - m_new);
       m_run = m_new;
@@ -203,26 +230,95 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
       for (int db = 0; db < DB; ++db) acc[db] *= alpha;
     }
     const float msub = (m_run == -INFINITY) ? 0.0f : m_run;
-    bf16x8 pb[4];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float e = need_mask ? fast_exp2(s[kb][i] - msub) : fast_exp2(fmaf(s[kb][i], cs, -msub));
-        l_run += e;
-        pb[kb * 2 + (i >> 3)][i & 7] = (bf16)e;
-      }
-    }
 
-    // ---- O^T += V^T P^T; chunk kc holds keys kb*32 + hh*16 + hc*8 + 0..7 for lane half hh ----
-    const int dsub = ((lane >> 4) & 1) * 16, i16 = lane & 15;
+    // first V fragments go out before the exponentials
+    bf16x8 va[4][DB];
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
-      const int row0 = (kc >> 1) * 32 + hh * 16 + (kc & 1) * 8;
+      const int rows = ((kc >> 1) * 32 + (kc & 1) * 8) * RB;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-        acc[db] = mfma32(lds_tr_frag<D>(vl, row0, db * 32 + dsub, i16), pb[kc], acc[db]);
+      for (int db = 0; db < DB; ++db) {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vl + voff[db][0] + rows));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vl + voff[db][1] + rows));
+        va[kc][db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
     }
+    bf16x8 pb[4];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float e0 = fast_exp2(fmaf(s0[i], cs, -msub));
+      const float e1 = fast_exp2(fmaf(s1[i], cs, -msub));
+      l_run += e0 + e1;
+      pb[i >> 3][i & 7] = (bf16)e0;
+      pb[2 + (i >> 3)][i & 7] = (bf16)e1;
+    }
+    // O^T += V^T P^T; chunk kc holds keys kb*32 + hh*16 + hc*8 + 0..7 for lane half hh
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[db] = mfma32(va[kc][db], pb[kc], acc[db]);
+    }
+    constexpr int PV = 4 * DB;                 // PV MFMAs, two transposed reads each
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 200, 0);
+#pragma unroll
+    for (int m = 0; m < PV - 4; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+  };
+
+  // Tile j lives in LDS stage j % 2; the copy of tile j+1 into the other stage is in flight while
+  // tile j is computed. Tiles [0, n_free) need no masking for any wave of the workgroup and run a
+  // body without mask code; the rest (causal diagonal, ragged tail, padded query rows) check per
+  // wave whether they see the tile at all and apply the element mask.
+  int n_free;
+  if constexpr (MASK == MASK_CAUSAL) {
+    n_free = min(q0 / BN, p.seq_k / BN);
+  } else if constexpr (MASK == MASK_PADDING) {
+    n_free = (q0 + BM <= q_len) ? kv_len / BN : 0;
+  } else if constexpr (MASK == MASK_BLOCK) {
+    n_free = (n_tiles > 0 && tile_index(n_tiles - 1) * BN + BN > p.seq_k) ? n_tiles - 1 : n_tiles;
+  } else {
+    n_free = p.seq_k / BN;
+  }
+  n_free = min(n_free, n_tiles);
+
+  auto step = [&](auto stage_tag, auto masked_tag, int j) __attribute__((always_inline)) {
+    constexpr int ST = decltype(stage_tag)::value;
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    wait_vmem();
+    __syncthreads();  // tile j is in LDS; every wave is done with the stage tile j+1 will overwrite
+    if (j + 1 < n_tiles) issue_tile(std::integral_constant<int, 1 - ST>{}, tile_index(j + 1));
+    const int k0 = tile_index(j) * BN;
+    if constexpr (!MASKED) {
+      tile(stage_tag, masked_tag, k0);
+    } else {
+      // wave-uniform: does this wave see any key of the tile?
+      bool active = k0 < kv_len;
+      if constexpr (MASK == MASK_CAUSAL) active = active && k0 <= qw0 + 31;
+      if constexpr (MASK == MASK_PADDING) active = active && qw0 < q_len;
+      if constexpr (MASK == MASK_BLOCK) active = ((list[j] >> 16) >> ((wave * 32) / 64)) & 1u;
+      if (active) tile(stage_tag, masked_tag, k0);
+    }
+  };
+  auto run = [&](auto masked_tag, int j0, int j1) __attribute__((always_inline)) {
+    int j = j0;
+    if (j < j1 && (j & 1)) step(std::integral_constant<int, 1>{}, masked_tag, j++);
+    for (; j + 1 < j1; j += 2) {
+      step(std::integral_constant<int, 0>{}, masked_tag, j);
+      step(std::integral_constant<int, 1>{}, masked_tag, j + 1);
+    }
+    if (j < j1) step(std::integral_constant<int, 0>{}, masked_tag, j);
+  };
+
+  if (n_tiles > 0) issue_tile(std::integral_constant<int, 0>{}, tile_index(0));
+  if constexpr (MASK == MASK_BLOCK && BM > 64) {
+    run(std::true_type{}, 0, n_tiles);   // waves of different layout rows may skip tiles
+  } else {
+    run(std::false_type{}, 0, n_free);
+    run(std::true_type{}, n_free, n_tiles);
   }
 
   // ---- epilogue: O = acc / l, LSE = ln 2 * (m + log2 l); empty rows give O = 0, LSE = -inf ----
@@ -248,27 +344,27 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
   }
 }
 
-template <int D, int NW, int MASK>
+#ifndef ATTN_FWD_NW
+#define ATTN_FWD_NW 4
+#endif
+#ifndef ATTN_FWD_MINW
+#define ATTN_FWD_MINW 2
+#endif
+
+template <int D, int NW, int MASK, int MINW>
 hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
-  static bool attr_done = false;
-  const int lds = FwdLds<D>::BYTES;
-  if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute((const void*)fwd_bf16_kernel<D, NW, MASK>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (e != hipSuccess) return e;
-    attr_done = true;
-  }
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, MASK>), dim3(p.n_items), dim3(NW * 64), lds, stream, p);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, MASK, MINW>), dim3(p.n_items), dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int D, int NW>
+template <int D>
 hipError_t launch_mask(const FwdParams& p, int mask, hipStream_t stream) {
+  constexpr int NW = ATTN_FWD_NW, MW = ATTN_FWD_MINW;
   switch (mask) {
-    case MASK_NONE: return launch_one<D, NW, MASK_NONE>(p, stream);
-    case MASK_CAUSAL: return launch_one<D, NW, MASK_CAUSAL>(p, stream);
-    case MASK_PADDING: return launch_one<D, NW, MASK_PADDING>(p, stream);
-    default: return launch_one<D, NW, MASK_BLOCK>(p, stream);
+    case MASK_NONE: return launch_one<D, NW, MASK_NONE, MW>(p, stream);
+    case MASK_CAUSAL: return launch_one<D, NW, MASK_CAUSAL, MW>(p, stream);
+    case MASK_PADDING: return launch_one<D, NW, MASK_PADDING, MW>(p, stream);
+    default: return launch_one<D, 2, MASK_BLOCK, 1>(p, stream);
   }
 }
 
@@ -276,13 +372,11 @@ hipError_t launch_mask(const FwdParams& p, int mask, hipStream_t stream) {
 
 int fwd_bf16_block_m(int head_dim, int mask) {
   (void)head_dim;
-  return mask == MASK_BLOCK ? 64 : 128;
+  return mask == MASK_BLOCK ? 64 : 32 * ATTN_FWD_NW;
 }
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int head_dim, int mask, hipStream_t stream) {
-  const int bm = fwd_bf16_block_m(head_dim, mask);
-  if (head_dim == 128) return bm == 64 ? launch_mask<128, 2>(p, mask, stream) : launch_mask<128, 4>(p, mask, stream);
-  return bm == 64 ? launch_mask<64, 2>(p, mask, stream) : launch_mask<64, 4>(p, mask, stream);
+  return head_dim == 128 ? launch_mask<128>(p, mask, stream) : launch_mask<64>(p, mask, stream);
 }
 
 }  // namespace attn

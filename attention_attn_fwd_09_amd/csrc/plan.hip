@@ -23,28 +23,45 @@ namespace {
 constexpr int NBUCKET = 4096;  // costs above this share the top bucket (order stays approximately LPT)
 constexpr int THREADS = 1024;
 
+constexpr int MAX_CACHED = 16384;  // items whose cost is kept in LDS between the passes
+
+// Number of kept tiles in the union of `nrows` consecutive layout rows starting at r0. The loads
+// are issued 16 at a time so that their latencies overlap (one dependent load per column would
+// make this prologue cost tens of microseconds).
 __device__ int layout_row_union_count(const uint8_t* lay, int nb_k, int r0, int nrows, int nb_q) {
   int count = 0;
-  for (int j = 0; j < nb_k; ++j) {
-    bool keep = false;
+  for (int j = 0; j < nb_k; j += 16) {
+    uint32_t keep = 0;
     for (int r = 0; r < nrows; ++r) {
       const int row = r0 + r;
-      if (row < nb_q && lay[(size_t)row * nb_k + j] != 0) keep = true;
+      if (row >= nb_q) break;
+      const uint8_t* rp = lay + (size_t)row * nb_k;
+      uint8_t v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] = (j + u < nb_k) ? rp[j + u] : (uint8_t)0;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) keep |= (v[u] != 0 ? 1u : 0u) << u;
     }
-    count += keep ? 1 : 0;
+    count += __popc(keep);
   }
   return count;
 }
 
+// Number of kept tiles in the union of `ncols` consecutive layout columns starting at c0.
 __device__ int layout_col_union_count(const uint8_t* lay, int nb_k, int c0, int ncols, int nb_q) {
   int count = 0;
-  for (int i = 0; i < nb_q; ++i) {
-    bool keep = false;
+  for (int i = 0; i < nb_q; i += 16) {
+    uint32_t keep = 0;
     for (int cc = 0; cc < ncols; ++cc) {
       const int col = c0 + cc;
-      if (col < nb_k && lay[(size_t)i * nb_k + col] != 0) keep = true;
+      if (col >= nb_k) break;
+      uint8_t v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] = (i + u < nb_q) ? lay[(size_t)(i + u) * nb_k + col] : (uint8_t)0;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) keep |= (v[u] != 0 ? 1u : 0u) << u;
     }
-    count += keep ? 1 : 0;
+    count += __popc(keep);
   }
   return count;
 }
@@ -116,11 +133,14 @@ __device__ int block_exclusive_scan(int v, int* wave_sums) {
 __global__ __launch_bounds__(THREADS) void plan_kernel(PlanParams p) {
   __shared__ int bucket[NBUCKET];
   __shared__ int wave_sums[THREADS / 64];
+  __shared__ uint16_t cached[MAX_CACHED];
+  const bool cache = p.n_items <= MAX_CACHED;
   for (int i = threadIdx.x; i < NBUCKET; i += THREADS) bucket[i] = 0;
   __syncthreads();
   // bucket r holds cost NBUCKET-1-r, so ascending r is descending cost
   for (int i = threadIdx.x; i < p.n_items; i += THREADS) {
     const int cost = min(item_cost(p, (uint32_t)i), NBUCKET - 1);
+    if (cache) cached[i] = (uint16_t)cost;
     atomicAdd(&bucket[NBUCKET - 1 - cost], 1);
   }
   __syncthreads();
@@ -140,7 +160,7 @@ __global__ __launch_bounds__(THREADS) void plan_kernel(PlanParams p) {
   }
   __syncthreads();
   for (int i = threadIdx.x; i < p.n_items; i += THREADS) {
-    const int cost = min(item_cost(p, (uint32_t)i), NBUCKET - 1);
+    const int cost = cache ? (int)cached[i] : min(item_cost(p, (uint32_t)i), NBUCKET - 1);
     const int pos = atomicAdd(&bucket[NBUCKET - 1 - cost], 1);
     p.items[pos] = (uint32_t)i;
   }
