@@ -20,6 +20,8 @@
 // Skipped blocks of a block-sparse layout (and fully masked causal/padding tiles) are never
 // visited. Every product runs on v_mfma_f32_32x32x16_bf16; operands that must be read along the
 // contraction dimension of a row-major tile come from LDS through ds_read_b64_tr_b16.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -55,15 +57,13 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int64_t rows)
 }
 
 // ------------------------------------------------------------------------------------------------
-// dK/dV pass.
+// dK/dV pass. Steps are (query head of the group, 64-row query tile) pairs; those that need no
+// element mask for any wave of the workgroup come first and run a body without mask code.
 template <int D>
 struct KvLds {
   static constexpr int TILE = BQ * D * 2;
-  static constexpr int STATS = 1024;                        // LSE (bytes 0..255) then zero fill
-  static constexpr int STAGE = 2 * TILE + 2 * STATS;        // Q, dO, LSE block, Delta block
-  static constexpr int LIST_OFF = 2 * STAGE;
-  static constexpr int MAX_STEPS = 4096;                    // (query head, query tile) pairs
-  static constexpr int BYTES = LIST_OFF + MAX_STEPS * 2 + 16;
+  static constexpr int STATS = 1024;        // 64 row values (256 B) plus the zero fill of the copy
+  static constexpr int MAX_STEPS = 4096;    // listed (query head, layout row) pairs for block masks
 };
 
 template <int D, int NW, int MASK>
@@ -71,10 +71,22 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int BK = NW * 32;   // keys per workgroup
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
+  constexpr int RB = D * 2;
   using L = KvLds<D>;
-  extern __shared__ __attribute__((aligned(16))) char smem[];
+  __shared__ __attribute__((aligned(16))) char q_st0[L::TILE];
+  __shared__ __attribute__((aligned(16))) char o_st0[L::TILE];   // dO
+  __shared__ __attribute__((aligned(16))) char q_st1[L::TILE];
+  __shared__ __attribute__((aligned(16))) char o_st1[L::TILE];
+  __shared__ __attribute__((aligned(16))) char l_st0[L::STATS];  // LSE
+  __shared__ __attribute__((aligned(16))) char d_st0[L::STATS];  // Delta
+  __shared__ __attribute__((aligned(16))) char l_st1[L::STATS];
+  __shared__ __attribute__((aligned(16))) char d_st1[L::STATS];
+  __shared__ uint16_t list[MASK == MASK_BLOCK ? L::MAX_STEPS : 1];
+  __shared__ int list_count;
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 31, hh = lane >> 5;
   const int dsub = ((lane >> 4) & 1) * 16, i16 = lane & 15;
 
@@ -87,14 +99,14 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdParams p) {
   const int my_k = kw0 + c;
 
   const size_t kv_off = ((size_t)(b * p.heads_kv + kvh) * p.seq_k) * D;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const bf16*)p.k + kv_off, (uint32_t)p.seq_k * D * 2);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const bf16*)p.v + kv_off, (uint32_t)p.seq_k * D * 2);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const bf16*)p.k + kv_off, (uint32_t)p.seq_k * RB);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const bf16*)p.v + kv_off, (uint32_t)p.seq_k * RB);
 
   // K and V rows of this lane's key: B operands of S = Q K^T and dP = dO V^T
   bf16x8 kf[KS], vf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    const uint32_t off = (uint32_t)my_k * (D * 2) + (uint32_t)(ks * 32 + hh * 16);
+    const uint32_t off = (uint32_t)my_k * RB + (uint32_t)(ks * 32 + hh * 16);
     kf[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
     vf[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
   }
@@ -103,10 +115,23 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdParams p) {
   int kv_len = p.seq_k, q_len = p.seq_q;
   const int n_qt = (p.seq_q + BQ - 1) / BQ;
   int qt_lo = 0, qt_hi = n_qt;
-  int n_steps;
-  uint16_t* list = (uint16_t*)(smem + L::LIST_OFF);
+  if constexpr (MASK == MASK_PADDING) {
+    kv_len = clamp_len(p.lengths[b], p.seq_k);
+    q_len = clamp_len(p.lengths[b], p.seq_q);
+    qt_hi = (k0 < kv_len) ? (q_len + BQ - 1) / BQ : 0;
+  } else if constexpr (MASK == MASK_CAUSAL) {
+    qt_lo = k0 / BQ;
+  }
+  const bool key_tail = k0 + BK > kv_len;    // some key of the tile is past the end
+  // query tiles [qt_m, qt_f) need no mask; [qt_lo, qt_m) (causal diagonal) and the ragged last
+  // tile [qt_f, qt_hi) do
+  int qt_m = qt_lo, qt_f = qt_hi;
+  if constexpr (MASK == MASK_CAUSAL) qt_m = min(qt_hi, max(qt_lo, (k0 + BK - 2) / BQ + 1));
+  if (qt_hi > qt_m && (qt_hi * BQ > q_len)) qt_f = qt_hi - 1;
+  if (key_tail) qt_f = qt_m;                 // every step masked
+  qt_f = max(qt_f, qt_m);
+  int n_free, n_steps;
   if constexpr (MASK == MASK_BLOCK) {
-    // kept layout rows of column k0/64 (BK == 64 for block masks), for each query head of the group
     const int col = k0 / 64;
     if (wave == 0) {
       int count = 0;
@@ -121,51 +146,73 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdParams p) {
           count += __popcll(ball);
         }
       }
-      if (lane == 0) *(int*)(smem + L::LIST_OFF + L::MAX_STEPS * 2) = min(count, L::MAX_STEPS);
+      if (lane == 0) list_count = min(count, L::MAX_STEPS);
     }
     __syncthreads();
-    n_steps = *(const int*)(smem + L::LIST_OFF + L::MAX_STEPS * 2);
+    n_steps = list_count;
+    // ragged shapes run every step through the masked body
+    n_free = (key_tail || (p.seq_q % BQ) != 0) ? 0 : n_steps;
   } else {
-    if constexpr (MASK == MASK_PADDING) {
-      kv_len = clamp_len(p.lengths[b], p.seq_k);
-      q_len = clamp_len(p.lengths[b], p.seq_q);
-      qt_hi = (k0 < kv_len) ? (q_len + BQ - 1) / BQ : 0;
-    } else if constexpr (MASK == MASK_CAUSAL) {
-      qt_lo = k0 / BQ;
-    }
-    n_steps = p.group * max(qt_hi - qt_lo, 0);
+    n_free = p.group * (qt_f - qt_m);
+    n_steps = p.group * (qt_hi - qt_lo);
   }
-  auto step_at = [&](int s, int& g, int& qt) {
+  auto step_at = [&](int s, int& g, int& qt) __attribute__((always_inline)) {
     if constexpr (MASK == MASK_BLOCK) {
       const uint32_t e = list[s];
       g = (int)(e >> 10);
       qt = (int)(e & 1023u);
     } else {
-      const int per = qt_hi - qt_lo;
-      g = s / per;
-      qt = qt_lo + s % per;
+      if (s < n_free) {
+        const int per = qt_f - qt_m;
+        g = s / per;
+        qt = qt_m + s % per;
+      } else {
+        // masked tiles: the causal diagonal [qt_lo, qt_m) then the tail [qt_f, qt_hi)
+        const int r = s - n_free;
+        const int per = (qt_m - qt_lo) + (qt_hi - qt_f);
+        g = r / per;
+        const int m = r % per;
+        qt = m < qt_m - qt_lo ? qt_lo + m : qt_f + (m - (qt_m - qt_lo));
+      }
     }
   };
 
-  auto issue_step = [&](char* stage, int s) {
+  auto issue_step = [&](auto stage_tag, int s) __attribute__((always_inline)) {
+    constexpr int ST = decltype(stage_tag)::value;
     int g, qt;
     step_at(s, g, qt);
     const int hq = kvh * p.group + g;
     const size_t q_off = ((size_t)(b * p.heads_q + hq) * p.seq_q) * D;
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc((const bf16*)p.q + q_off, (uint32_t)p.seq_q * D * 2);
-    const __amdgpu_buffer_rsrc_t rdo = make_rsrc((const bf16*)p.dout + q_off, (uint32_t)p.seq_q * D * 2);
-    issue_rows<D, NW>(stage, rq, qt * BQ, wave, lane);
-    issue_rows<D, NW>(stage + L::TILE, rdo, qt * BQ, wave, lane);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc((const bf16*)p.q + q_off, (uint32_t)p.seq_q * RB);
+    const __amdgpu_buffer_rsrc_t rdo = make_rsrc((const bf16*)p.dout + q_off, (uint32_t)p.seq_q * RB);
+    issue_rows<D, NW>(ST == 0 ? q_st0 : q_st1, rq, qt * BQ, wave, lane);
+    issue_rows<D, NW>(ST == 0 ? o_st0 : o_st1, rdo, qt * BQ, wave, lane);
     if (wave == 0) {
       const size_t r_off = (size_t)(b * p.heads_q + hq) * p.seq_q;
       const __amdgpu_buffer_rsrc_t rl = make_rsrc(p.lse + r_off, (uint32_t)p.seq_q * 4);
       const __amdgpu_buffer_rsrc_t rd = make_rsrc(p.delta + r_off, (uint32_t)p.seq_q * 4);
       // lanes 0-15 fetch the 64 row values; the others point past the buffer and write zeros
       const uint32_t off = lane < 16 ? (uint32_t)(qt * BQ + lane * 4) * 4 : 0x80000000u;
-      buffer_to_lds16(rl, stage + 2 * L::TILE, off);
-      buffer_to_lds16(rd, stage + 2 * L::TILE + L::STATS, off);
+      buffer_to_lds16(rl, ST == 0 ? l_st0 : l_st1, off);
+      buffer_to_lds16(rd, ST == 0 ? d_st0 : d_st1, off);
     }
   };
+
+  // per-lane LDS offsets inside a 64-row Q/dO tile: row fragments of query block qb (rows
+  // qb*32 + sigma32(c)) and transposed fragments (rows qb*32 + hh*16 + hc*8 + 0..7)
+  int roff[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) roff[ks] = sigma32(c) * RB + (((2 * ks + hh) ^ swz<D>(sigma32(c))) * 16);
+  int toff[DB][2];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int row = hh * 16 + half * 4 + (i16 >> 2);
+      const int d = db * 32 + dsub + 4 * (i16 & 3);
+      toff[db][half] = row * RB + (((d >> 3) ^ swz<D>(row)) * 16) + (d & 7) * 2;
+    }
+  }
 
   f32x16 dk[DB], dv[DB];
 #pragma unroll
@@ -175,69 +222,100 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdParams p) {
   }
   const float cs = p.scale_log2;
 
-  if (n_steps > 0) issue_step(smem, 0);
-  for (int s = 0; s < n_steps; ++s) {
-    wait_vmem();
-    __syncthreads();
-    if (s + 1 < n_steps) issue_step(smem + ((s + 1) & 1) * L::STAGE, s + 1);
-
-    int g, qt;
-    step_at(s, g, qt);
-    const int q0 = qt * BQ;
-    bool active = kw0 < kv_len;
-    bool need_mask = (q0 + BQ > q_len) || (kw0 + 32 > kv_len);
-    if constexpr (MASK == MASK_CAUSAL) {
-      active = active && kw0 <= q0 + BQ - 1;
-      need_mask = need_mask || (kw0 + 31 > q0);
-    } else if constexpr (MASK == MASK_PADDING) {
-      active = active && q0 < q_len;
-    }
-    if (!active) continue;
-
-    const char* ql = smem + (s & 1) * L::STAGE;
-    const char* dol = ql + L::TILE;
-    const float* lse_l = (const float*)(ql + 2 * L::TILE);
-    const float* del_l = (const float*)(ql + 2 * L::TILE + L::STATS);
-
+  auto body = [&](auto stage_tag, auto masked_tag, int q0) __attribute__((always_inline)) {
+    constexpr int ST = decltype(stage_tag)::value;
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const char* ql = ST == 0 ? q_st0 : q_st1;
+    const char* dol = ST == 0 ? o_st0 : o_st1;
+    const float* lse_l = (const float*)(ST == 0 ? l_st0 : l_st1);
+    const float* del_l = (const float*)(ST == 0 ? d_st0 : d_st1);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       // S and dP for 32 queries x this wave's 32 keys; lane (c, hh) holds key my_k and queries
       // q0 + qb*32 + hh*16 + i
       f32x16 sc = f32x16{}, dp = f32x16{};
+      bf16x8 qa[KS], oa[KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const int row = qb * 32 + sigma32(c);
-        sc = mfma32(lds_row_frag<D>(ql, row, 2 * ks + hh), kf[ks], sc);
-        dp = mfma32(lds_row_frag<D>(dol, row, 2 * ks + hh), vf[ks], dp);
+        qa[ks] = *(const bf16x8*)(ql + roff[ks] + qb * 32 * RB);
+        oa[ks] = *(const bf16x8*)(dol + roff[ks] + qb * 32 * RB);
       }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        sc = mfma32(qa[ks], kf[ks], sc);
+        dp = mfma32(oa[ks], vf[ks], dp);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int ks = 0; ks < KS - 2; ++ks) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+
       const int qbase = qb * 32 + hh * 16;
       bf16x8 pb[2], dsb[2];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float lse2 = lse_to_log2(lse_l[qbase + i]);
         float pv = fast_exp2(fmaf(sc[i], cs, -lse2));
-        if (need_mask) {
+        if constexpr (MASKED) {
           const int q = q0 + qbase + i;
           bool vis = q < q_len && my_k < kv_len;
           if constexpr (MASK == MASK_CAUSAL) vis = vis && my_k <= q;
           pv = vis ? pv : 0.0f;
         }
-        const float dsv = pv * (dp[i] - del_l[qbase + i]);
         pb[i >> 3][i & 7] = (bf16)pv;
-        dsb[i >> 3][i & 7] = (bf16)dsv;
+        dsb[i >> 3][i & 7] = (bf16)(pv * (dp[i] - del_l[qbase + i]));
       }
       // dV += P^T dO and dK += dS^T Q: rows = this wave's keys, contraction over the 32 queries
 #pragma unroll
       for (int hc = 0; hc < 2; ++hc) {
-        const int row0 = qb * 32 + hh * 16 + hc * 8;
+        const int rows = (qb * 32 + hc * 8) * RB;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          dv[db] = mfma32(pb[hc], lds_tr_frag<D>(dol, row0, db * 32 + dsub, i16), dv[db]);
-          dk[db] = mfma32(dsb[hc], lds_tr_frag<D>(ql, row0, db * 32 + dsub, i16), dk[db]);
+          const i16x4 olo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, dol + toff[db][0] + rows));
+          const i16x4 ohi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, dol + toff[db][1] + rows));
+          const i16x4 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, ql + toff[db][0] + rows));
+          const i16x4 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, ql + toff[db][1] + rows));
+          dv[db] = mfma32(pb[hc], __builtin_bit_cast(bf16x8, __builtin_shufflevector(olo, ohi, 0, 1, 2, 3, 4, 5, 6, 7)), dv[db]);
+          dk[db] = mfma32(dsb[hc], __builtin_bit_cast(bf16x8, __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7)), dk[db]);
         }
       }
     }
-  }
+  };
+
+  auto step = [&](auto stage_tag, auto masked_tag, int s) __attribute__((always_inline)) {
+    constexpr int ST = decltype(stage_tag)::value;
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    wait_vmem();
+    __syncthreads();
+    if (s + 1 < n_steps) issue_step(std::integral_constant<int, 1 - ST>{}, s + 1);
+    int g, qt;
+    step_at(s, g, qt);
+    const int q0 = qt * BQ;
+    if constexpr (!MASKED) {
+      body(stage_tag, masked_tag, q0);
+    } else {
+      bool active = kw0 < kv_len;
+      if constexpr (MASK == MASK_CAUSAL) active = active && kw0 <= q0 + BQ - 1;
+      if constexpr (MASK == MASK_PADDING) active = active && q0 < q_len;
+      if (active) body(stage_tag, masked_tag, q0);
+    }
+  };
+  auto run = [&](auto masked_tag, int s0, int s1) __attribute__((always_inline)) {
+    int s = s0;
+    if (s < s1 && (s & 1)) step(std::integral_constant<int, 1>{}, masked_tag, s++);
+    for (; s + 1 < s1; s += 2) {
+      step(std::integral_constant<int, 0>{}, masked_tag, s);
+      step(std::integral_constant<int, 1>{}, masked_tag, s + 1);
+    }
+    if (s < s1) step(std::integral_constant<int, 0>{}, masked_tag, s);
+  };
+
+  if (n_steps > 0) issue_step(std::integral_constant<int, 0>{}, 0);
+  run(std::false_type{}, 0, n_free);
+  run(std::true_type{}, n_free, n_steps);
 
   // ---- write dK (times scale) and dV; lane (c, hh) holds column db*32 + c of keys kw0 + row ----
   bf16* dkg = (bf16*)p.dk + kv_off;
@@ -256,25 +334,30 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdParams p) {
 }
 
 // ------------------------------------------------------------------------------------------------
-// dQ pass.
+// dQ pass: same tile loop as the forward kernel (K and V tiles double-buffered in four separately
+// named LDS arrays, per-lane precomputed swizzled offsets, mask-free tiles in their own loop).
 template <int D>
 struct QLds {
   static constexpr int TILE = BN * D * 2;
-  static constexpr int STAGE = 2 * TILE;   // K, V
-  static constexpr int LIST_OFF = 2 * STAGE;
   static constexpr int MAX_LIST = 1024;
-  static constexpr int BYTES = LIST_OFF + MAX_LIST * 4 + 16;
 };
 
-template <int D, int NW, int MASK>
-__global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdParams p) {
+template <int D, int NW, int MASK, int MINW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW))) void bwd_dq_kernel(BwdParams p) {
   constexpr int BM = NW * 32;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
+  constexpr int RB = D * 2;
   using L = QLds<D>;
-  extern __shared__ __attribute__((aligned(16))) char smem[];
+  __shared__ __attribute__((aligned(16))) char k_st0[L::TILE];
+  __shared__ __attribute__((aligned(16))) char v_st0[L::TILE];
+  __shared__ __attribute__((aligned(16))) char k_st1[L::TILE];
+  __shared__ __attribute__((aligned(16))) char v_st1[L::TILE];
+  __shared__ uint32_t list[MASK == MASK_BLOCK ? L::MAX_LIST + 1 : 1];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 31, hh = lane >> 5;
   const int dsub = ((lane >> 4) & 1) * 16, i16 = lane & 15;
 
@@ -286,14 +369,13 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdParams p) {
 
   const size_t q_off = ((size_t)(b * p.heads_q + h) * p.seq_q) * D;
   const size_t kv_off = ((size_t)(b * p.heads_kv + kvh) * p.seq_k) * D;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const bf16*)p.q + q_off, (uint32_t)p.seq_q * D * 2);
-  const __amdgpu_buffer_rsrc_t rdo = make_rsrc((const bf16*)p.dout + q_off, (uint32_t)p.seq_q * D * 2);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const bf16*)p.k + kv_off, (uint32_t)p.seq_k * D * 2);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const bf16*)p.v + kv_off, (uint32_t)p.seq_k * D * 2);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const bf16*)p.q + q_off, (uint32_t)p.seq_q * RB);
+  const __amdgpu_buffer_rsrc_t rdo = make_rsrc((const bf16*)p.dout + q_off, (uint32_t)p.seq_q * RB);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const bf16*)p.k + kv_off, (uint32_t)p.seq_k * RB);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const bf16*)p.v + kv_off, (uint32_t)p.seq_k * RB);
 
   int kv_len = p.seq_k, q_len = p.seq_q;
   int n_tiles;
-  uint32_t* list = (uint32_t*)(smem + L::LIST_OFF);
   if constexpr (MASK == MASK_PADDING) {
     kv_len = clamp_len(p.lengths[b], p.seq_k);
     q_len = clamp_len(p.lengths[b], p.seq_q);
@@ -333,7 +415,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdParams p) {
   bf16x8 qf[KS], dof[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    const uint32_t off = (uint32_t)my_q * (D * 2) + (uint32_t)(ks * 32 + hh * 16);
+    const uint32_t off = (uint32_t)my_q * RB + (uint32_t)(ks * 32 + hh * 16);
     qf[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
     dof[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rdo, off, 0, 0));
   }
@@ -341,73 +423,142 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdParams p) {
   const float lse2 = my_q < p.seq_q ? lse_to_log2(p.lse[row_off + my_q]) : INFINITY;
   const float delta = my_q < p.seq_q ? p.delta[row_off + my_q] : 0.0f;
 
+  // per-lane LDS offsets: row fragments (K and V tiles share the layout) and transposed K reads
+  int roff[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) roff[ks] = sigma32(c) * RB + (((2 * ks + hh) ^ swz<D>(sigma32(c))) * 16);
+  int toff[DB][2];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int row = hh * 16 + half * 4 + (i16 >> 2);
+      const int d = db * 32 + dsub + 4 * (i16 & 3);
+      toff[db][half] = row * RB + (((d >> 3) ^ swz<D>(row)) * 16) + (d & 7) * 2;
+    }
+  }
+
   f32x16 acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
   const float cs = p.scale_log2;
 
-  auto tile_index = [&](int j) -> int {
+  auto tile_index = [&](int j) __attribute__((always_inline)) -> int {
     if constexpr (MASK == MASK_BLOCK) return (int)(list[j] & 0xffffu);
     return j;
   };
-  auto issue_tile = [&](char* stage, int kt) {
-    issue_rows<D, NW>(stage, rk, kt * BN, wave, lane);
-    issue_rows<D, NW>(stage + L::TILE, rv, kt * BN, wave, lane);
+  auto issue_tile = [&](auto stage_tag, int kt) __attribute__((always_inline)) {
+    constexpr int ST = decltype(stage_tag)::value;
+    issue_rows<D, NW>(ST == 0 ? k_st0 : k_st1, rk, kt * BN, wave, lane);
+    issue_rows<D, NW>(ST == 0 ? v_st0 : v_st1, rv, kt * BN, wave, lane);
   };
-  if (n_tiles > 0) issue_tile(smem, tile_index(0));
 
-  for (int j = 0; j < n_tiles; ++j) {
-    wait_vmem();
-    __syncthreads();
-    if (j + 1 < n_tiles) issue_tile(smem + ((j + 1) & 1) * L::STAGE, tile_index(j + 1));
-
-    const int k0 = tile_index(j) * BN;
-    bool active = true, need_mask = (k0 + BN > kv_len);
-    if constexpr (MASK == MASK_CAUSAL) {
-      active = k0 <= qw0 + 31;
-      need_mask = need_mask || (k0 + BN - 1 > qw0);
-    } else if constexpr (MASK == MASK_PADDING) {
-      active = qw0 < q_len;
-      need_mask = need_mask || (qw0 + 31 >= q_len);
-    } else if constexpr (MASK == MASK_BLOCK) {
-      active = ((list[j] >> 16) >> ((wave * 32) / 64)) & 1u;
-    }
-    if (!active) continue;
-
-    const char* kl = smem + (j & 1) * L::STAGE;
-    const char* vl = kl + L::TILE;
-    f32x16 sc[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int row = kb * 32 + sigma32(c);
-        sc[kb] = mfma32(lds_row_frag<D>(kl, row, 2 * ks + hh), qf[ks], sc[kb]);
-        dp[kb] = mfma32(lds_row_frag<D>(vl, row, 2 * ks + hh), dof[ks], dp[kb]);
-      }
-    }
-    bf16x8 dsb[4];
+  // One 64-key tile, processed as two 32-key halves: S^T and dP^T of the half, then dS, then the
+  // dQ^T += K^T dS^T contributions of its two 16-key chunks.
+  auto tile = [&](auto stage_tag, auto masked_tag, int k0) __attribute__((always_inline)) {
+    constexpr int ST = decltype(stage_tag)::value;
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const char* kl = ST == 0 ? k_st0 : k_st1;
+    const char* vl = ST == 0 ? v_st0 : v_st1;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      f32x16 sc = f32x16{}, dp = f32x16{};
+      bf16x8 ka[KS], va[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        ka[ks] = *(const bf16x8*)(kl + roff[ks] + kb * 32 * RB);
+        va[ks] = *(const bf16x8*)(vl + roff[ks] + kb * 32 * RB);
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        sc = mfma32(ka[ks], qf[ks], sc);
+        dp = mfma32(va[ks], dof[ks], dp);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int ks = 0; ks < KS - 2; ++ks) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+
+      // transposed K fragments for this half's two chunks go out before the element-wise work
+      bf16x8 kt[2][DB];
+#pragma unroll
+      for (int hc = 0; hc < 2; ++hc) {
+        const int rows = (kb * 32 + hc * 8) * RB;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, kl + toff[db][0] + rows));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, kl + toff[db][1] + rows));
+          kt[hc][db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+      }
+      bf16x8 dsb[2];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float pv = fast_exp2(fmaf(sc[kb][i], cs, -lse2));
-        if (need_mask) {
+        float pv = fast_exp2(fmaf(sc[i], cs, -lse2));
+        if constexpr (MASKED) {
           const int key = k0 + kb * 32 + hh * 16 + i;
           bool vis = key < kv_len && my_q < q_len;
           if constexpr (MASK == MASK_CAUSAL) vis = vis && key <= my_q;
           pv = vis ? pv : 0.0f;
         }
-        dsb[kb * 2 + (i >> 3)][i & 7] = (bf16)(pv * (dp[kb][i] - delta));
+        dsb[i >> 3][i & 7] = (bf16)(pv * (dp[i] - delta));
+      }
+#pragma unroll
+      for (int hc = 0; hc < 2; ++hc) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[db] = mfma32(kt[hc][db], dsb[hc], acc[db]);
       }
     }
-    // dQ^T += K^T dS^T: A = K^T from the transposed read of the K tile
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      const int row0 = (kc >> 1) * 32 + hh * 16 + (kc & 1) * 8;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) acc[db] = mfma32(lds_tr_frag<D>(kl, row0, db * 32 + dsub, i16), dsb[kc], acc[db]);
+  };
+
+  int n_free;
+  if constexpr (MASK == MASK_CAUSAL) {
+    n_free = min(q0 / BN, p.seq_k / BN);
+  } else if constexpr (MASK == MASK_PADDING) {
+    n_free = (q0 + BM <= q_len) ? kv_len / BN : 0;
+  } else if constexpr (MASK == MASK_BLOCK) {
+    n_free = (n_tiles > 0 && tile_index(n_tiles - 1) * BN + BN > p.seq_k) ? n_tiles - 1 : n_tiles;
+  } else {
+    n_free = p.seq_k / BN;
+  }
+  n_free = min(n_free, n_tiles);
+
+  auto step = [&](auto stage_tag, auto masked_tag, int j) __attribute__((always_inline)) {
+    constexpr int ST = decltype(stage_tag)::value;
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    wait_vmem();
+    __syncthreads();
+    if (j + 1 < n_tiles) issue_tile(std::integral_constant<int, 1 - ST>{}, tile_index(j + 1));
+    const int k0 = tile_index(j) * BN;
+    if constexpr (!MASKED) {
+      tile(stage_tag, masked_tag, k0);
+    } else {
+      bool active = k0 < kv_len;
+      if constexpr (MASK == MASK_CAUSAL) active = active && k0 <= qw0 + 31;
+      if constexpr (MASK == MASK_PADDING) active = active && qw0 < q_len;
+      if constexpr (MASK == MASK_BLOCK) active = ((list[j] >> 16) >> ((wave * 32) / 64)) & 1u;
+      if (active) tile(stage_tag, masked_tag, k0);
     }
+  };
+  auto run = [&](auto masked_tag, int j0, int j1) __attribute__((always_inline)) {
+    int j = j0;
+    if (j < j1 && (j & 1)) step(std::integral_constant<int, 1>{}, masked_tag, j++);
+    for (; j + 1 < j1; j += 2) {
+      step(std::integral_constant<int, 0>{}, masked_tag, j);
+      step(std::integral_constant<int, 1>{}, masked_tag, j + 1);
+    }
+    if (j < j1) step(std::integral_constant<int, 0>{}, masked_tag, j);
+  };
+
+  if (n_tiles > 0) issue_tile(std::integral_constant<int, 0>{}, tile_index(0));
+  if constexpr (MASK == MASK_BLOCK && BM > 64) {
+    run(std::true_type{}, 0, n_tiles);
+  } else {
+    run(std::false_type{}, 0, n_free);
+    run(std::true_type{}, n_free, n_tiles);
   }
 
   if (my_q < p.seq_q) {
@@ -426,29 +577,15 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdParams p) {
 }
 
 // ------------------------------------------------------------------------------------------------
-template <typename K>
-hipError_t set_lds(K kernel, int bytes, bool& done) {
-  if (done) return hipSuccess;
-  hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-  if (e == hipSuccess) done = true;
-  return e;
-}
-
 template <int D, int NW, int MASK>
 hipError_t launch_dkdv_one(const BwdParams& p, int n_items, hipStream_t s) {
-  static bool done = false;
-  hipError_t e = set_lds(bwd_dkdv_kernel<D, NW, MASK>, KvLds<D>::BYTES, done);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, MASK>), dim3(n_items), dim3(NW * 64), KvLds<D>::BYTES, s, p);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, MASK>), dim3(n_items), dim3(NW * 64), 0, s, p);
   return hipGetLastError();
 }
 
-template <int D, int NW, int MASK>
+template <int D, int NW, int MASK, int MINW>
 hipError_t launch_dq_one(const BwdParams& p, int n_items, hipStream_t s) {
-  static bool done = false;
-  hipError_t e = set_lds(bwd_dq_kernel<D, NW, MASK>, QLds<D>::BYTES, done);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, NW, MASK>), dim3(n_items), dim3(NW * 64), QLds<D>::BYTES, s, p);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, NW, MASK, MINW>), dim3(n_items), dim3(NW * 64), 0, s, p);
   return hipGetLastError();
 }
 
@@ -465,10 +602,10 @@ hipError_t dkdv_mask(const BwdParams& p, int mask, int n_items, hipStream_t s) {
 template <int D>
 hipError_t dq_mask(const BwdParams& p, int mask, int n_items, hipStream_t s) {
   switch (mask) {
-    case MASK_NONE: return launch_dq_one<D, 4, MASK_NONE>(p, n_items, s);
-    case MASK_CAUSAL: return launch_dq_one<D, 4, MASK_CAUSAL>(p, n_items, s);
-    case MASK_PADDING: return launch_dq_one<D, 4, MASK_PADDING>(p, n_items, s);
-    default: return launch_dq_one<D, 2, MASK_BLOCK>(p, n_items, s);
+    case MASK_NONE: return launch_dq_one<D, 4, MASK_NONE, 2>(p, n_items, s);
+    case MASK_CAUSAL: return launch_dq_one<D, 4, MASK_CAUSAL, 2>(p, n_items, s);
+    case MASK_PADDING: return launch_dq_one<D, 4, MASK_PADDING, 2>(p, n_items, s);
+    default: return launch_dq_one<D, 2, MASK_BLOCK, 2>(p, n_items, s);
   }
 }
 

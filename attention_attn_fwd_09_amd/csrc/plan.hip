@@ -66,20 +66,32 @@ __device__ int layout_col_union_count(const uint8_t* lay, int nb_k, int c0, int 
   return count;
 }
 
-__device__ int item_cost(const PlanParams& p, uint32_t item) {
+constexpr int MAX_UNITS = 4096;   // layout rows/columns whose cost is tabulated once in LDS
+constexpr int MAX_LENGTHS = 4096; // padding lengths cached in LDS
+
+struct PlanShared {
+  int unit_cost[MAX_UNITS];       // shared block layout: kept tiles per layout row (or column)
+  int lengths[MAX_LENGTHS];
+};
+
+// Cost of one item. `tab` says whether sh.unit_cost holds the shared layout's per-row (FWD_Q) or
+// per-column (BWD_KV) counts, and whether sh.lengths holds the padding lengths.
+__device__ int item_cost(const PlanParams& p, uint32_t item, const PlanShared& sh, bool tab_units, bool tab_len) {
   const int t = (int)(item % (uint32_t)p.n_tiles);
   const uint32_t bh = item / (uint32_t)p.n_tiles;
   const int h = (int)(bh % (uint32_t)p.heads);
   const int b = (int)(bh / (uint32_t)p.heads);
   const int tile = p.tile;
+  const int len = (p.mask == MASK_PADDING) ? (tab_len ? sh.lengths[b] : p.lengths[b]) : 0;
   if (p.mode == PLAN_BWD_KV) {
     // key tile t of kv head h
     if (p.mask == MASK_PADDING) {
-      const int L = clamp_len(p.lengths[b], p.seq_k);
-      const int Lq = clamp_len(p.lengths[b], p.seq_q);
+      const int L = clamp_len(len, p.seq_k);
+      const int Lq = clamp_len(len, p.seq_q);
       return (t * tile < L) ? p.group * ((Lq + 63) / 64) : 0;
     }
     if (p.mask == MASK_BLOCK) {
+      if (tab_units) return p.group * sh.unit_cost[(t * tile) / 64];
       int total = 0;
       for (int g = 0; g < p.group; ++g) {
         const int hq = h * p.group + g;
@@ -93,11 +105,12 @@ __device__ int item_cost(const PlanParams& p, uint32_t item) {
   }
   // query tile t of query head h
   if (p.mask == MASK_PADDING) {
-    const int L = clamp_len(p.lengths[b], p.seq_k);
-    const int Lq = clamp_len(p.lengths[b], p.seq_q);
+    const int L = clamp_len(len, p.seq_k);
+    const int Lq = clamp_len(len, p.seq_q);
     return (t * tile < Lq) ? (L + 63) / 64 : 0;
   }
   if (p.mask == MASK_BLOCK) {
+    if (tab_units) return sh.unit_cost[(t * tile) / 64];
     const uint8_t* lay = p.layout + b * p.layout_stride_b + h * p.layout_stride_h;
     return layout_row_union_count(lay, p.nb_k, (t * tile) / 64, tile > 64 ? tile / 64 : 1, p.nb_q);
   }
@@ -134,12 +147,37 @@ __global__ __launch_bounds__(THREADS) void plan_kernel(PlanParams p) {
   __shared__ int bucket[NBUCKET];
   __shared__ int wave_sums[THREADS / 64];
   __shared__ uint16_t cached[MAX_CACHED];
+  __shared__ PlanShared sh;
   const bool cache = p.n_items <= MAX_CACHED;
+  // A block layout shared by every (batch, head) with one layout row (or column) per tile: count
+  // each row's (column's) kept tiles once, every thread taking independent bytes of the layout.
+  const bool tab_units = p.mask == MASK_BLOCK && p.layout_stride_b == 0 && p.layout_stride_h == 0 &&
+                         p.tile == 64 && (p.mode == PLAN_BWD_KV ? p.nb_k : p.nb_q) <= MAX_UNITS;
+  const bool tab_len = p.mask == MASK_PADDING && p.n_items > 0 &&
+                       (int64_t)p.n_items / ((int64_t)p.heads * p.n_tiles) <= MAX_LENGTHS;
   for (int i = threadIdx.x; i < NBUCKET; i += THREADS) bucket[i] = 0;
+  if (tab_units) {
+    const int n_units = p.mode == PLAN_BWD_KV ? p.nb_k : p.nb_q;
+    for (int u = threadIdx.x; u < n_units; u += THREADS) sh.unit_cost[u] = 0;
+  }
+  if (tab_len) {
+    const int batch = (int)((int64_t)p.n_items / ((int64_t)p.heads * p.n_tiles));
+    for (int b = threadIdx.x; b < batch; b += THREADS) sh.lengths[b] = p.lengths[b];
+  }
   __syncthreads();
+  if (tab_units) {
+    const int64_t total = (int64_t)p.nb_q * p.nb_k;
+    for (int64_t e = threadIdx.x; e < total; e += THREADS) {
+      if (p.layout[e] != 0) {
+        const int unit = p.mode == PLAN_BWD_KV ? (int)(e % p.nb_k) : (int)(e / p.nb_k);
+        atomicAdd(&sh.unit_cost[unit], 1);
+      }
+    }
+    __syncthreads();
+  }
   // bucket r holds cost NBUCKET-1-r, so ascending r is descending cost
   for (int i = threadIdx.x; i < p.n_items; i += THREADS) {
-    const int cost = min(item_cost(p, (uint32_t)i), NBUCKET - 1);
+    const int cost = min(item_cost(p, (uint32_t)i, sh, tab_units, tab_len), NBUCKET - 1);
     if (cache) cached[i] = (uint16_t)cost;
     atomicAdd(&bucket[NBUCKET - 1 - cost], 1);
   }
@@ -160,7 +198,7 @@ __global__ __launch_bounds__(THREADS) void plan_kernel(PlanParams p) {
   }
   __syncthreads();
   for (int i = threadIdx.x; i < p.n_items; i += THREADS) {
-    const int cost = cache ? (int)cached[i] : min(item_cost(p, (uint32_t)i), NBUCKET - 1);
+    const int cost = cache ? (int)cached[i] : min(item_cost(p, (uint32_t)i, sh, tab_units, tab_len), NBUCKET - 1);
     const int pos = atomicAdd(&bucket[NBUCKET - 1 - cost], 1);
     p.items[pos] = (uint32_t)i;
   }
