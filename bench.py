@@ -219,6 +219,16 @@ def run_gpu(args):
 
     if args.all:
         forward_all(lib, torch, dev, WORKLOADS, workload_inputs)
+    if args.copy_mib:
+        # a plain device copy of known size: hardware byte counters read for it calibrate the
+        # counters read for the attention kernels
+        n = args.copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = n
     return result
 
 
@@ -289,6 +299,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all", action="store_true", help="also print forward timings of every workload to stderr")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after the timed steps, run one device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the attention path here is built and "
