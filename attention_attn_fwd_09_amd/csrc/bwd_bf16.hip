@@ -254,21 +254,16 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdParams p) {
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 
       const int qbase = qb * 32 + hh * 16;
-      bf16x8 pb[2], dsb[2];
+      // row statistics of this lane's 16 queries, and every transposed fragment of the dV/dK
+      // products, go out before the element-wise work (the pass runs one wave per SIMD, so LDS
+      // latency has to be covered inside the wave)
+      f32x4 lse4[4], del4[4];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float lse2 = lse_to_log2(lse_l[qbase + i]);
-        float pv = fast_exp2(fmaf(sc[i], cs, -lse2));
-        if constexpr (MASKED) {
-          const int q = q0 + qbase + i;
-          bool vis = q < q_len && my_k < kv_len;
-          if constexpr (MASK == MASK_CAUSAL) vis = vis && my_k <= q;
-          pv = vis ? pv : 0.0f;
-        }
-        pb[i >> 3][i & 7] = (bf16)pv;
-        dsb[i >> 3][i & 7] = (bf16)(pv * (dp[i] - del_l[qbase + i]));
+      for (int r = 0; r < 4; ++r) {
+        lse4[r] = *(const f32x4*)(lse_l + qbase + 4 * r);
+        del4[r] = *(const f32x4*)(del_l + qbase + 4 * r);
       }
-      // dV += P^T dO and dK += dS^T Q: rows = this wave's keys, contraction over the 32 queries
+      bf16x8 ot[2][DB], qt[2][DB];
 #pragma unroll
       for (int hc = 0; hc < 2; ++hc) {
         const int rows = (qb * 32 + hc * 8) * RB;
@@ -278,10 +273,43 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdParams p) {
           const i16x4 ohi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, dol + toff[db][1] + rows));
           const i16x4 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, ql + toff[db][0] + rows));
           const i16x4 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, ql + toff[db][1] + rows));
-          dv[db] = mfma32(pb[hc], __builtin_bit_cast(bf16x8, __builtin_shufflevector(olo, ohi, 0, 1, 2, 3, 4, 5, 6, 7)), dv[db]);
-          dk[db] = mfma32(dsb[hc], __builtin_bit_cast(bf16x8, __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7)), dk[db]);
+          ot[hc][db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(olo, ohi, 0, 1, 2, 3, 4, 5, 6, 7));
+          qt[hc][db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7));
         }
       }
+      bf16x8 pb[2], dsb[2];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float lse2 = lse_to_log2(lse4[i >> 2][i & 3]);
+        float pv = fast_exp2(fmaf(sc[i], cs, -lse2));
+        if constexpr (MASKED) {
+          const int q = q0 + qbase + i;
+          bool vis = q < q_len && my_k < kv_len;
+          if constexpr (MASK == MASK_CAUSAL) vis = vis && my_k <= q;
+          pv = vis ? pv : 0.0f;
+        }
+        pb[i >> 3][i & 7] = (bf16)pv;
+        dsb[i >> 3][i & 7] = (bf16)(pv * (dp[i] - del4[i >> 2][i & 3]));
+      }
+      // dV += P^T dO and dK += dS^T Q: rows = this wave's keys, contraction over the 32 queries
+#pragma unroll
+      for (int hc = 0; hc < 2; ++hc) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          dv[db] = mfma32(pb[hc], ot[hc][db], dv[db]);
+          dk[db] = mfma32(dsb[hc], qt[hc][db], dk[db]);
+        }
+      }
+      // schedule: stats and the first chunk's transposed reads, the vector work, then the second
+      // chunk's reads interleaved with the first chunk's MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, 8 + 4 * DB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 400, 0);
+#pragma unroll
+      for (int m = 0; m < 2 * DB; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * DB, 0);
     }
   };
 
@@ -534,7 +562,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
     if (j + 1 < n_tiles) issue_tile(std::integral_constant<int, 1 - ST>{}, tile_index(j + 1));
     const int k0 = tile_index(j) * BN;
     if constexpr (!MASKED) {
-      tile(stage_tag, masked_tag, k0);
+      bool active = true;
+      if constexpr (MASK == MASK_BLOCK && BM > 64) active = ((list[j] >> 16) >> ((wave * 32) / 64)) & 1u;
+      if (active) tile(stage_tag, masked_tag, k0);
     } else {
       bool active = k0 < kv_len;
       if constexpr (MASK == MASK_CAUSAL) active = active && k0 <= qw0 + 31;
@@ -554,12 +584,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
   };
 
   if (n_tiles > 0) issue_tile(std::integral_constant<int, 0>{}, tile_index(0));
-  if constexpr (MASK == MASK_BLOCK && BM > 64) {
-    run(std::true_type{}, 0, n_tiles);
-  } else {
-    run(std::false_type{}, 0, n_free);
-    run(std::true_type{}, n_free, n_tiles);
-  }
+  run(std::false_type{}, 0, n_free);
+  run(std::true_type{}, n_free, n_tiles);
 
   if (my_q < p.seq_q) {
     bf16* dqg = (bf16*)p.dq + q_off + (size_t)my_q * D;
@@ -605,15 +631,16 @@ hipError_t dq_mask(const BwdParams& p, int mask, int n_items, hipStream_t s) {
     case MASK_NONE: return launch_dq_one<D, 4, MASK_NONE, 2>(p, n_items, s);
     case MASK_CAUSAL: return launch_dq_one<D, 4, MASK_CAUSAL, 2>(p, n_items, s);
     case MASK_PADDING: return launch_dq_one<D, 4, MASK_PADDING, 2>(p, n_items, s);
-    default: return launch_dq_one<D, 2, MASK_BLOCK, 2>(p, n_items, s);
+    default: return launch_dq_one<D, 4, MASK_BLOCK, 2>(p, n_items, s);
   }
 }
 
 }  // namespace
 
-// Tile sizes: the block-sparse layout works on 64 x 64 tiles, so its passes use 64-row tiles
-// (2 waves); other masks use 128-row tiles (4 waves).
-int bwd_block_q(int head_dim, int mask) { (void)head_dim; return mask == MASK_BLOCK ? 64 : 128; }
+// Tile sizes: dQ items are 128 query rows (4 waves; a block layout's two rows are listed as the
+// union of their kept tiles and each wave pair computes only its own row's). dK/dV items are 128
+// keys, or one 64-key layout column for block masks (2 waves).
+int bwd_block_q(int head_dim, int mask) { (void)head_dim; (void)mask; return 128; }
 int bwd_block_k(int head_dim, int mask) { (void)head_dim; return mask == MASK_BLOCK ? 64 : 128; }
 int bwd_max_steps() { return KvLds<128>::MAX_STEPS; }
 

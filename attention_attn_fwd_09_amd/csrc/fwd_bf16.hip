@@ -293,7 +293,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
     if (j + 1 < n_tiles) issue_tile(std::integral_constant<int, 1 - ST>{}, tile_index(j + 1));
     const int k0 = tile_index(j) * BN;
     if constexpr (!MASKED) {
-      tile(stage_tag, masked_tag, k0);
+      bool active = true;
+      if constexpr (MASK == MASK_BLOCK && BM > 64) active = ((list[j] >> 16) >> ((wave * 32) / 64)) & 1u;
+      if (active) tile(stage_tag, masked_tag, k0);
     } else {
       // wave-uniform: does this wave see any key of the tile?
       bool active = k0 < kv_len;
@@ -314,12 +316,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
   };
 
   if (n_tiles > 0) issue_tile(std::integral_constant<int, 0>{}, tile_index(0));
-  if constexpr (MASK == MASK_BLOCK && BM > 64) {
-    run(std::true_type{}, 0, n_tiles);   // waves of different layout rows may skip tiles
-  } else {
-    run(std::false_type{}, 0, n_free);
-    run(std::true_type{}, n_free, n_tiles);
-  }
+  run(std::false_type{}, 0, n_free);
+  run(std::true_type{}, n_free, n_tiles);
 
   // ---- epilogue: O = acc / l, LSE = ln 2 * (m + log2 l); empty rows give O = 0, LSE = -inf ----
   const float l = partner_sum(l_run);
@@ -364,7 +362,7 @@ hipError_t launch_mask(const FwdParams& p, int mask, hipStream_t stream) {
     case MASK_NONE: return launch_one<D, NW, MASK_NONE, MW>(p, stream);
     case MASK_CAUSAL: return launch_one<D, NW, MASK_CAUSAL, MW>(p, stream);
     case MASK_PADDING: return launch_one<D, NW, MASK_PADDING, MW>(p, stream);
-    default: return launch_one<D, 2, MASK_BLOCK, 1>(p, stream);
+    default: return launch_one<D, 4, MASK_BLOCK, 2>(p, stream);
   }
 }
 
@@ -372,7 +370,7 @@ hipError_t launch_mask(const FwdParams& p, int mask, hipStream_t stream) {
 
 int fwd_bf16_block_m(int head_dim, int mask) {
   (void)head_dim;
-  return mask == MASK_BLOCK ? 64 : 32 * ATTN_FWD_NW;
+  return mask == MASK_BLOCK ? 128 : 32 * ATTN_FWD_NW;
 }
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int head_dim, int mask, hipStream_t stream) {

@@ -20,7 +20,9 @@ namespace attn {
 
 namespace {
 
-constexpr int NBUCKET = 4096;  // costs above this share the top bucket (order stays approximately LPT)
+constexpr int NXCD = 8;        // workgroup i is dispatched to XCD i % 8
+constexpr int NCOST = 1024;   // cost buckets per XCD; larger costs share the top bucket
+constexpr int NBUCKET = NXCD * NCOST;
 constexpr int THREADS = 1024;
 
 constexpr int MAX_CACHED = 16384;  // items whose cost is kept in LDS between the passes
@@ -66,7 +68,7 @@ __device__ int layout_col_union_count(const uint8_t* lay, int nb_k, int c0, int 
   return count;
 }
 
-constexpr int MAX_UNITS = 4096;   // layout rows/columns whose cost is tabulated once in LDS
+constexpr int MAX_UNITS = 4096;   // tiles whose cost is tabulated once in LDS (shared block layouts)
 constexpr int MAX_LENGTHS = 4096; // padding lengths cached in LDS
 
 struct PlanShared {
@@ -91,7 +93,7 @@ __device__ int item_cost(const PlanParams& p, uint32_t item, const PlanShared& s
       return (t * tile < L) ? p.group * ((Lq + 63) / 64) : 0;
     }
     if (p.mask == MASK_BLOCK) {
-      if (tab_units) return p.group * sh.unit_cost[(t * tile) / 64];
+      if (tab_units) return p.group * sh.unit_cost[t];
       int total = 0;
       for (int g = 0; g < p.group; ++g) {
         const int hq = h * p.group + g;
@@ -110,7 +112,7 @@ __device__ int item_cost(const PlanParams& p, uint32_t item, const PlanShared& s
     return (t * tile < Lq) ? (L + 63) / 64 : 0;
   }
   if (p.mask == MASK_BLOCK) {
-    if (tab_units) return sh.unit_cost[(t * tile) / 64];
+    if (tab_units) return sh.unit_cost[t];
     const uint8_t* lay = p.layout + b * p.layout_stride_b + h * p.layout_stride_h;
     return layout_row_union_count(lay, p.nb_k, (t * tile) / 64, tile > 64 ? tile / 64 : 1, p.nb_q);
   }
@@ -149,37 +151,51 @@ __global__ __launch_bounds__(THREADS) void plan_kernel(PlanParams p) {
   __shared__ uint16_t cached[MAX_CACHED];
   __shared__ PlanShared sh;
   const bool cache = p.n_items <= MAX_CACHED;
-  // A block layout shared by every (batch, head) with one layout row (or column) per tile: count
-  // each row's (column's) kept tiles once, every thread taking independent bytes of the layout.
+  // A block layout shared by every (batch, head): the cost of a tile is the number of kept
+  // columns (rows) in the union of its layout rows (columns), the same for every (batch, head).
+  // Tabulate it once, every thread testing independent (tile, column) pairs of the layout.
+  const int per_unit = p.tile / 64;                   // layout rows (columns) per tile
+  const int n_other = p.mode == PLAN_BWD_KV ? p.nb_q : p.nb_k;
   const bool tab_units = p.mask == MASK_BLOCK && p.layout_stride_b == 0 && p.layout_stride_h == 0 &&
-                         p.tile == 64 && (p.mode == PLAN_BWD_KV ? p.nb_k : p.nb_q) <= MAX_UNITS;
+                         per_unit >= 1 && p.n_tiles <= MAX_UNITS;
   const bool tab_len = p.mask == MASK_PADDING && p.n_items > 0 &&
                        (int64_t)p.n_items / ((int64_t)p.heads * p.n_tiles) <= MAX_LENGTHS;
   for (int i = threadIdx.x; i < NBUCKET; i += THREADS) bucket[i] = 0;
-  if (tab_units) {
-    const int n_units = p.mode == PLAN_BWD_KV ? p.nb_k : p.nb_q;
-    for (int u = threadIdx.x; u < n_units; u += THREADS) sh.unit_cost[u] = 0;
-  }
+  if (tab_units)
+    for (int u = threadIdx.x; u < p.n_tiles; u += THREADS) sh.unit_cost[u] = 0;
   if (tab_len) {
     const int batch = (int)((int64_t)p.n_items / ((int64_t)p.heads * p.n_tiles));
     for (int b = threadIdx.x; b < batch; b += THREADS) sh.lengths[b] = p.lengths[b];
   }
   __syncthreads();
   if (tab_units) {
-    const int64_t total = (int64_t)p.nb_q * p.nb_k;
+    const int64_t total = (int64_t)p.n_tiles * n_other;
     for (int64_t e = threadIdx.x; e < total; e += THREADS) {
-      if (p.layout[e] != 0) {
-        const int unit = p.mode == PLAN_BWD_KV ? (int)(e % p.nb_k) : (int)(e / p.nb_k);
-        atomicAdd(&sh.unit_cost[unit], 1);
+      const int unit = (int)(e / n_other), x = (int)(e % n_other);
+      bool keep = false;
+      for (int r = 0; r < per_unit; ++r) {
+        const int y = unit * per_unit + r;
+        if (p.mode == PLAN_BWD_KV) {
+          if (y < p.nb_k && p.layout[(size_t)x * p.nb_k + y] != 0) keep = true;
+        } else {
+          if (y < p.nb_q && p.layout[(size_t)y * p.nb_k + x] != 0) keep = true;
+        }
       }
+      if (keep) atomicAdd(&sh.unit_cost[unit], 1);
     }
     __syncthreads();
   }
-  // bucket r holds cost NBUCKET-1-r, so ascending r is descending cost
+  // Items of one (batch, kv-head) unit share K and V (forward, dQ) or Q and dO (dK/dV); when the
+  // units divide evenly over the XCDs, unit u goes to XCD u % 8 so that its data stay in one L2.
+  // Within an XCD items are ordered longest first. Bucket xcd * NCOST + (NCOST - 1 - cost).
+  const int items_per_unit = p.mode == PLAN_BWD_KV ? p.n_tiles : p.group * p.n_tiles;
+  const int n_units = p.n_items / items_per_unit;
+  const bool spread = (n_units % NXCD) == 0;
+  auto xcd_of = [&](int i) { return spread ? (i / items_per_unit) % NXCD : 0; };
   for (int i = threadIdx.x; i < p.n_items; i += THREADS) {
-    const int cost = min(item_cost(p, (uint32_t)i, sh, tab_units, tab_len), NBUCKET - 1);
+    const int cost = min(item_cost(p, (uint32_t)i, sh, tab_units, tab_len), NCOST - 1);
     if (cache) cached[i] = (uint16_t)cost;
-    atomicAdd(&bucket[NBUCKET - 1 - cost], 1);
+    atomicAdd(&bucket[xcd_of(i) * NCOST + NCOST - 1 - cost], 1);
   }
   __syncthreads();
   constexpr int PER = NBUCKET / THREADS;
@@ -197,10 +213,12 @@ __global__ __launch_bounds__(THREADS) void plan_kernel(PlanParams p) {
     off += local[k];
   }
   __syncthreads();
+  const int per_xcd = spread ? p.n_items / NXCD : p.n_items;
   for (int i = threadIdx.x; i < p.n_items; i += THREADS) {
-    const int cost = cache ? (int)cached[i] : min(item_cost(p, (uint32_t)i, sh, tab_units, tab_len), NBUCKET - 1);
-    const int pos = atomicAdd(&bucket[NBUCKET - 1 - cost], 1);
-    p.items[pos] = (uint32_t)i;
+    const int cost = cache ? (int)cached[i] : min(item_cost(p, (uint32_t)i, sh, tab_units, tab_len), NCOST - 1);
+    const int x = xcd_of(i);
+    const int rank = atomicAdd(&bucket[x * NCOST + NCOST - 1 - cost], 1) - x * per_xcd;
+    p.items[spread ? rank * NXCD + x : rank] = (uint32_t)i;
   }
 }
 
