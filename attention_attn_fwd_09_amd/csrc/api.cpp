@@ -89,7 +89,7 @@ size_t fwd_ws(const attn_problem* p, const attn_mask* m) {
 struct BwdSizes {
   int bq, bk, n_qt, n_kt;
   int64_t q_items, kv_items;
-  size_t delta_off, kv_off, q_off, total;
+  size_t delta_off, lse2_off, kv_off, q_off, total;
 };
 
 BwdSizes bwd_sizes(const attn_problem* p, const attn_mask* m) {
@@ -101,7 +101,8 @@ BwdSizes bwd_sizes(const attn_problem* p, const attn_mask* m) {
   s.q_items = (int64_t)p->batch * p->heads_q * s.n_qt;
   s.kv_items = (int64_t)p->batch * p->heads_kv * s.n_kt;
   s.delta_off = 0;
-  s.kv_off = align_up((size_t)p->batch * p->heads_q * p->seq_q * 4);
+  s.lse2_off = align_up((size_t)p->batch * p->heads_q * p->seq_q * 4);
+  s.kv_off = s.lse2_off + align_up((size_t)p->batch * p->heads_q * p->seq_q * 4);
   s.q_off = s.kv_off + align_up((size_t)s.kv_items * 4);
   s.total = s.q_off + align_up((size_t)s.q_items * 4);
   return s;
@@ -319,6 +320,7 @@ attn_status attn_bwd(const attn_problem* problem, const void* Q, const void* K, 
   bp.q = Q; bp.k = K; bp.v = V; bp.o = O; bp.dout = dO; bp.lse = LSE;
   bp.dq = dQ; bp.dk = dK; bp.dv = dV;
   bp.delta = (float*)(ws + bs.delta_off);
+  bp.lse2 = (float*)(ws + bs.lse2_off);
   bp.lengths = m->lengths; bp.layout = m->block_layout;
   bp.layout_stride_b = m->layout_stride_b; bp.layout_stride_h = m->layout_stride_h;
   bp.items_kv = (const uint32_t*)(ws + bs.kv_off);

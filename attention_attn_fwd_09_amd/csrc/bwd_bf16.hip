@@ -8,7 +8,8 @@
 // and must resolve write conflicts. This file takes the two-loop option (no output atomics, a
 // deterministic result):
 //
-//   preprocess  Delta_i = sum_d dO_id O_id (equal to sum_j P_ij dP_ij; fp32, one value per row)
+//   preprocess  Delta_i = sum_d dO_id O_id (equal to sum_j P_ij dP_ij; fp32, one value per row,
+//               stored negated so that it can seed the dP accumulators)
 //   dK/dV pass  one workgroup per key tile: K_j, V_j stay in registers, every (query head of the
 //               group, query tile) that sees the tile streams Q_i, dO_i, LSE_i, Delta_i through
 //               LDS; S = Q_i K_j^T and dP = dO_i V_j^T are recomputed, P = exp(scale S - LSE),
@@ -38,7 +39,8 @@ constexpr float LOG2E = 1.4426950408889634f;
 __device__ __forceinline__ float lse_to_log2(float l) { return l == -INFINITY ? INFINITY : l * LOG2E; }
 
 // ------------------------------------------------------------------------------------------------
-// Preprocess: Delta = rowsum(dO * O), one group of D/8 lanes per row (16 bytes per lane).
+// Preprocess: -Delta = -rowsum(dO * O), one group of D/8 lanes per row (16 bytes per lane), and
+// the row's LSE in the log2 domain (so the two passes subtract it without converting per element).
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int64_t rows) {
   constexpr int LPR = D / 8;
@@ -53,7 +55,10 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int64_t rows)
   }
 #pragma unroll
   for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
-  if (row < rows && sub == 0) p.delta[row] = acc;
+  if (row < rows && sub == 0) {
+    p.delta[row] = -acc;
+    p.lse2[row] = lse_to_log2(p.lse[row]);
+  }
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -77,8 +82,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) char o_st0[L::TILE];   // dO
   __shared__ __attribute__((aligned(16))) char q_st1[L::TILE];
   __shared__ __attribute__((aligned(16))) char o_st1[L::TILE];
-  __shared__ __attribute__((aligned(16))) char l_st0[L::STATS];  // LSE
-  __shared__ __attribute__((aligned(16))) char d_st0[L::STATS];  // Delta
+  __shared__ __attribute__((aligned(16))) char l_st0[L::STATS];  // LSE * log2(e)
+  __shared__ __attribute__((aligned(16))) char d_st0[L::STATS];  // -Delta
   __shared__ __attribute__((aligned(16))) char l_st1[L::STATS];
   __shared__ __attribute__((aligned(16))) char d_st1[L::STATS];
   __shared__ uint16_t list[MASK == MASK_BLOCK ? L::MAX_STEPS : 1];
@@ -189,7 +194,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdParams p) {
     issue_rows<D, NW>(ST == 0 ? o_st0 : o_st1, rdo, qt * BQ, wave, lane);
     if (wave == 0) {
       const size_t r_off = (size_t)(b * p.heads_q + hq) * p.seq_q;
-      const __amdgpu_buffer_rsrc_t rl = make_rsrc(p.lse + r_off, (uint32_t)p.seq_q * 4);
+      const __amdgpu_buffer_rsrc_t rl = make_rsrc(p.lse2 + r_off, (uint32_t)p.seq_q * 4);
       const __amdgpu_buffer_rsrc_t rd = make_rsrc(p.delta + r_off, (uint32_t)p.seq_q * 4);
       // lanes 0-15 fetch the 64 row values; the others point past the buffer and write zeros
       const uint32_t off = lane < 16 ? (uint32_t)(qt * BQ + lane * 4) * 4 : 0x80000000u;
@@ -222,6 +227,11 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdParams p) {
   }
   const float cs = p.scale_log2;
 
+  // One step: 64 queries in two 32-row blocks. For block qb, S = Q K^T and dP - Delta (the dP
+  // accumulator starts at -Delta) are computed with this wave's 32 keys in the lane's column, then
+  // P = exp2(scale log2(e) S - LSE log2(e)) and dS = P (dP - Delta), then dV += P^T dO and
+  // dK += dS^T Q. The two blocks are software-pipelined so that the vector work of one block runs
+  // under the MFMAs of the other: [S,dP 0] [S,dP 1 | P,dS 0] [dV,dK 0 | P,dS 1] [dV,dK 1].
   auto body = [&](auto stage_tag, auto masked_tag, int q0) __attribute__((always_inline)) {
     constexpr int ST = decltype(stage_tag)::value;
     constexpr bool MASKED = decltype(masked_tag)::value;
@@ -229,41 +239,39 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdParams p) {
     const char* dol = ST == 0 ? o_st0 : o_st1;
     const float* lse_l = (const float*)(ST == 0 ? l_st0 : l_st1);
     const float* del_l = (const float*)(ST == 0 ? d_st0 : d_st1);
+
+    // row statistics of the lane's 16 queries qb*32 + hh*16 + 0..15, in MFMA accumulator order
+    auto stats = [&](int qb, f32x16& lse16, f32x16& nd16) __attribute__((always_inline)) {
+      const int qbase = qb * 32 + hh * 16;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      // S and dP for 32 queries x this wave's 32 keys; lane (c, hh) holds key my_k and queries
-      // q0 + qb*32 + hh*16 + i
-      f32x16 sc = f32x16{}, dp = f32x16{};
+      for (int r = 0; r < 4; ++r) {
+        const f32x4 l4 = *(const f32x4*)(lse_l + qbase + 4 * r);
+        const f32x4 d4 = *(const f32x4*)(del_l + qbase + 4 * r);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          lse16[4 * r + e] = l4[e];
+          nd16[4 * r + e] = d4[e];
+        }
+      }
+    };
+    // S and dP - Delta of block qb; lane (c, hh) holds key my_k and queries qb*32 + hh*16 + i
+    auto scores = [&](int qb, const f32x16& nd16, f32x16& sc, f32x16& dp) __attribute__((always_inline)) {
       bf16x8 qa[KS], oa[KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         qa[ks] = *(const bf16x8*)(ql + roff[ks] + qb * 32 * RB);
         oa[ks] = *(const bf16x8*)(dol + roff[ks] + qb * 32 * RB);
       }
+      sc = f32x16{};
+      dp = nd16;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         sc = mfma32(qa[ks], kf[ks], sc);
         dp = mfma32(oa[ks], vf[ks], dp);
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-      for (int ks = 0; ks < KS - 2; ++ks) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-
-      const int qbase = qb * 32 + hh * 16;
-      // row statistics of this lane's 16 queries, and every transposed fragment of the dV/dK
-      // products, go out before the element-wise work (the pass runs one wave per SIMD, so LDS
-      // latency has to be covered inside the wave)
-      f32x4 lse4[4], del4[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        lse4[r] = *(const f32x4*)(lse_l + qbase + 4 * r);
-        del4[r] = *(const f32x4*)(del_l + qbase + 4 * r);
-      }
-      bf16x8 ot[2][DB], qt[2][DB];
+    };
+    // transposed dO and Q fragments of block qb (B operands of the dV and dK products)
+    auto tr_frags = [&](int qb, bf16x8 (&ot)[2][DB], bf16x8 (&qt)[2][DB]) __attribute__((always_inline)) {
 #pragma unroll
       for (int hc = 0; hc < 2; ++hc) {
         const int rows = (qb * 32 + hc * 8) * RB;
@@ -277,21 +285,26 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdParams p) {
           qt[hc][db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7));
         }
       }
-      bf16x8 pb[2], dsb[2];
+    };
+    // P and dS of block qb in bf16 (A operands of the dV and dK products)
+    auto probs = [&](int qb, const f32x16& sc, const f32x16& dp, const f32x16& lse16, bf16x8 (&pb)[2],
+                     bf16x8 (&dsb)[2]) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float lse2 = lse_to_log2(lse4[i >> 2][i & 3]);
-        float pv = fast_exp2(fmaf(sc[i], cs, -lse2));
+        float pv = fast_exp2(fmaf(sc[i], cs, -lse16[i]));
         if constexpr (MASKED) {
-          const int q = q0 + qbase + i;
+          const int q = q0 + qb * 32 + hh * 16 + i;
           bool vis = q < q_len && my_k < kv_len;
           if constexpr (MASK == MASK_CAUSAL) vis = vis && my_k <= q;
           pv = vis ? pv : 0.0f;
         }
         pb[i >> 3][i & 7] = (bf16)pv;
-        dsb[i >> 3][i & 7] = (bf16)(pv * (dp[i] - del4[i >> 2][i & 3]));
+        dsb[i >> 3][i & 7] = (bf16)(pv * dp[i]);
       }
-      // dV += P^T dO and dK += dS^T Q: rows = this wave's keys, contraction over the 32 queries
+    };
+    // dV += P^T dO and dK += dS^T Q: rows = this wave's keys, contraction over the 32 queries
+    auto grads = [&](const bf16x8 (&pb)[2], const bf16x8 (&dsb)[2], const bf16x8 (&ot)[2][DB],
+                     const bf16x8 (&qt)[2][DB]) __attribute__((always_inline)) {
 #pragma unroll
       for (int hc = 0; hc < 2; ++hc) {
 #pragma unroll
@@ -300,17 +313,51 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdParams p) {
           dk[db] = mfma32(dsb[hc], qt[hc][db], dk[db]);
         }
       }
-      // schedule: stats and the first chunk's transposed reads, the vector work, then the second
-      // chunk's reads interleaved with the first chunk's MFMAs
-      __builtin_amdgcn_sched_group_barrier(0x100, 8 + 4 * DB, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 400, 0);
+    };
+
+    constexpr int NM = 2 * KS;   // MFMAs of scores(); grads() has 4 * DB
+    f32x16 lse0, nd0, lse1, nd1, sc0, dp0, sc1, dp1;
+    bf16x8 ot0[2][DB], qt0[2][DB], ot1[2][DB], qt1[2][DB];
+    bf16x8 pb0[2], ds0[2], pb1[2], ds1[2];
+
+    // [S,dP 0]: statistics first (the dP chain starts from -Delta), fragment reads two k-steps ahead
+    stats(0, lse0, nd0);
+    scores(0, nd0, sc0, dp0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8 + 4, 0);
 #pragma unroll
-      for (int m = 0; m < 2 * DB; ++m) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 2 * DB, 0);
+    for (int m = 0; m < KS - 2; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+
+    // [S,dP 1 | P,dS 0]: block 1's statistics and fragments, block 0's transposed fragments
+    stats(1, lse1, nd1);
+    scores(1, nd1, sc1, dp1);
+    tr_frags(0, ot0, qt0);
+    probs(0, sc0, dp0, lse0, pb0, ds0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8 + 4, 0);
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+    }
+
+    // [dV,dK 0 | P,dS 1]: block 1's transposed fragments replace block 0's as they are consumed
+    tr_frags(1, ot1, qt1);
+    grads(pb0, ds0, ot0, qt0);
+    probs(1, sc1, dp1, lse1, pb1, ds1);
+#pragma unroll
+    for (int m = 0; m < 4 * DB; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+    }
+
+    // [dV,dK 1]
+    grads(pb1, ds1, ot1, qt1);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * DB, 0);
   };
 
   auto step = [&](auto stage_tag, auto masked_tag, int s) __attribute__((always_inline)) {
@@ -448,8 +495,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
     dof[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rdo, off, 0, 0));
   }
   const size_t row_off = (size_t)(b * p.heads_q + h) * p.seq_q;
-  const float lse2 = my_q < p.seq_q ? lse_to_log2(p.lse[row_off + my_q]) : INFINITY;
-  const float delta = my_q < p.seq_q ? p.delta[row_off + my_q] : 0.0f;
+  const float lse2 = my_q < p.seq_q ? p.lse2[row_off + my_q] : INFINITY;
+  const float ndelta = my_q < p.seq_q ? p.delta[row_off + my_q] : 0.0f;   // -Delta
 
   // per-lane LDS offsets: row fragments (K and V tiles share the layout) and transposed K reads
   int roff[KS];
@@ -532,7 +579,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
           if constexpr (MASK == MASK_CAUSAL) vis = vis && key <= my_q;
           pv = vis ? pv : 0.0f;
         }
-        dsb[i >> 3][i & 7] = (bf16)(pv * (dp[i] - delta));
+        dsb[i >> 3][i & 7] = (bf16)(pv * (dp[i] + ndelta));
       }
 #pragma unroll
       for (int hc = 0; hc < 2; ++hc) {

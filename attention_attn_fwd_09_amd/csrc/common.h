@@ -124,11 +124,24 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 // in the 32x32 output each half-wave holds 16 consecutive keys of its query column.
 __device__ __forceinline__ int sigma32(int r) { return ((r >> 2) & 1) * 16 + (r >> 3) * 4 + (r & 3); }
 
+// NaN-propagating maximum (v_maximum3_f32 on gfx950). fmaxf would first quiet every operand the
+// compiler cannot prove canonical (one extra VALU op per MFMA result).
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+// acc + sum of the 8 bf16 values of x, in fp32, four v_dot2 ops against (1, 1)
+__device__ __forceinline__ float sum_bf16x8(bf16x8 x, float acc) {
+  const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 0, 1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 2, 3), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 4, 5), one, acc, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 6, 7), one, acc, false);
+}
+
 // --- wavefront helpers ---
 __device__ __forceinline__ float partner_max(float x) {
   // value of lane l^32 combined with our own: permlane32_swap(x, x) returns {x[l], x[l^32]} in some order.
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float partner_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

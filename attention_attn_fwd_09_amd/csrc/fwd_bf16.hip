@@ -153,7 +153,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
   float m_run = -INFINITY;   // reference maximum, log2 domain (scores times scale*log2(e))
-  float l_run = 0.0f;        // this lane's partial denominator (its 16 keys of each 32-key block)
+  float l_run = 0.0f;        // this lane's partial denominators (its 16 keys of the first and of
+  float l_run2 = 0.0f;       // the second 32-key block of every tile)
   const float cs = p.scale_log2;
 
   auto tile_index = [&](int j) __attribute__((always_inline)) -> int {
@@ -219,13 +220,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
     // ---- online softmax on this lane's 32 scores (keys k0 + kb*32 + hh*16 + i) ----
     float mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
+    for (int i = 0; i < 16; ++i) mx = vmax(mx, vmax(s0[i], s1[i]));
     mx = partner_max(mx) * cs;   // cs > 0, so max(s) * cs = max(s * cs); -inf stays -inf
     if (__builtin_expect(__ballot(mx > m_run + RESCALE_SLACK) != 0, 0)) {
-      const float m_new = fmaxf(m_run, mx);
+      const float m_new = vmax(m_run, mx);
       const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
+      l_run2 *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) acc[db] *= alpha;
     }
@@ -248,10 +250,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
     for (int i = 0; i < 16; ++i) {
       const float e0 = fast_exp2(fmaf(s0[i], cs, -msub));
       const float e1 = fast_exp2(fmaf(s1[i], cs, -msub));
-      l_run += e0 + e1;
       pb[i >> 3][i & 7] = (bf16)e0;
       pb[2 + (i >> 3)][i & 7] = (bf16)e1;
     }
+    // the denominator sums the same bf16-rounded probabilities that enter P V
+    l_run = sum_bf16x8(pb[0], sum_bf16x8(pb[1], l_run));
+    l_run2 = sum_bf16x8(pb[2], sum_bf16x8(pb[3], l_run2));
     // O^T += V^T P^T; chunk kc holds keys kb*32 + hh*16 + hc*8 + 0..7 for lane half hh
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
@@ -320,7 +324,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
   run(std::true_type{}, n_free, n_tiles);
 
   // ---- epilogue: O = acc / l, LSE = ln 2 * (m + log2 l); empty rows give O = 0, LSE = -inf ----
-  const float l = partner_sum(l_run);
+  const float l = partner_sum(l_run + l_run2);
   const bool empty = !(l > 0.0f);
   const float inv = empty ? 0.0f : __builtin_amdgcn_rcpf(l);
   if (my_q < p.seq_q) {

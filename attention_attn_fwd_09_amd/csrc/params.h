@@ -38,7 +38,8 @@ struct BwdParams {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;                 // workspace: rowsum(dO * O), fp32 [B, Hq, Sq]
+  float* delta;                 // workspace: -rowsum(dO * O) (negated Delta), fp32 [B, Hq, Sq]
+  float* lse2;                  // workspace: LSE * log2(e), +inf for empty rows, fp32 [B, Hq, Sq]
   const int32_t* lengths;
   const uint8_t* layout;
   int64_t layout_stride_b, layout_stride_h;

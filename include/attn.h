@@ -118,7 +118,7 @@ attn_status attn_fwd(const attn_problem *problem, const void *Q, const void *K, 
                      const attn_mask *mask, float scale, void *O, float *LSE,
                      void *workspace, size_t workspace_bytes, void *stream);
 
-/* Bytes of workspace attn_bwd needs (the planner lists and D = rowsum(dO * O)). */
+/* Bytes of workspace attn_bwd needs (the planner lists, D = rowsum(dO * O) and LSE * log2(e)). */
 size_t attn_bwd_workspace_bytes(const attn_problem *problem, const attn_mask *mask);
 
 /*
