@@ -84,6 +84,45 @@ def visible_pairs(w, inp) -> int:
     return int(per) * (1 if lay.dim() == 4 else b * hq)
 
 
+def library_sources_sha256() -> str:
+    """Hash of every source the HIP library is built from (kernels, C ABI, public header)."""
+    import hashlib
+
+    root = os.path.dirname(os.path.abspath(__file__))
+    csrc = os.path.join(root, "attention_attn_fwd_09_amd", "csrc")
+    files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc) if f.endswith((".hip", ".cpp", ".h")))
+    files.append(os.path.join(root, "include", "attn.h"))
+    h = hashlib.sha256()
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def hbm_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` on `workload` from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads for a plain copy of known
+    size), or None when no summary matches the sources this library is built from."""
+    root = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
+    if not os.path.isdir(root):
+        return None
+    digest = library_sources_sha256()
+    for name in sorted(os.listdir(root)):
+        if not name.endswith("_hbm_traffic.md"):
+            continue
+        with open(os.path.join(root, name)) as fh:
+            for line in fh:
+                if not line.startswith("traffic-record: "):
+                    continue
+                rec = json.loads(line[len("traffic-record: "):])
+                if rec.get("workload") == workload and rec.get("sources_sha256") == digest:
+                    k = rec.get("kernels", {}).get(kernel)
+                    if k is not None:
+                        return int(k["bytes_per_launch"])
+    return None
+
+
 def run_gpu(args):
     import torch
 
@@ -182,6 +221,8 @@ def run_gpu(args):
         achieved = kernel_bytes.get(dominant, 0) / (dom_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+    roofline["traffic"] = hbm_traffic(KERNEL_NAMES[dominant], w.name)
+    roofline["traffic_unit"] = "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
     roofline["kernel"] = KERNEL_NAMES[dominant]
     roofline["kernel_ms"] = round(dom_ms, 5)
 
