@@ -79,6 +79,12 @@ def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
     lib.attn_bwd_workspace_bytes.restype = sz
     lib.attn_fwd.argtypes = [pp, vp, vp, vp, pm, ctypes.c_float, vp, vp, vp, sz, vp]
     lib.attn_fwd.restype = ctypes.c_int
+    lib.attn_fwd_ex.argtypes = [pp, vp, vp, vp, pm, ctypes.c_float, vp, vp, vp, sz, ctypes.c_int32, vp]
+    lib.attn_fwd_ex.restype = ctypes.c_int
+    lib.attn_fwd_ex_workspace_bytes.argtypes = [pp, pm, ctypes.c_int32]
+    lib.attn_fwd_ex_workspace_bytes.restype = sz
+    lib.attn_fwd_kv_splits.argtypes = [pp, pm, ctypes.c_int32]
+    lib.attn_fwd_kv_splits.restype = ctypes.c_int32
     lib.attn_bwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, pm, ctypes.c_float, vp, vp, vp, vp, sz, vp]
     lib.attn_bwd.restype = ctypes.c_int
     lib.attn_status_string.argtypes = [ctypes.c_int]
@@ -157,10 +163,18 @@ def _raise(status: int):
         raise AttnError(status, attn_status_string(status))
 
 
-def attn_fwd_workspace_bytes(q: torch.Tensor, k: torch.Tensor, mask: Optional[Mask] = None) -> int:
+def attn_fwd_workspace_bytes(q: torch.Tensor, k: torch.Tensor, mask: Optional[Mask] = None,
+                             kv_splits: int = 0) -> int:
     lib = load_library()
     m = (mask or Mask()).to_c()
-    return int(lib.attn_fwd_workspace_bytes(ctypes.byref(_problem(q, k)), ctypes.byref(m)))
+    return int(lib.attn_fwd_ex_workspace_bytes(ctypes.byref(_problem(q, k)), ctypes.byref(m), int(kv_splits)))
+
+
+def attn_fwd_kv_splits(q: torch.Tensor, k: torch.Tensor, mask: Optional[Mask] = None, kv_splits: int = 0) -> int:
+    """Number of key-range splits attn_fwd would use (0 for an invalid problem)."""
+    lib = load_library()
+    m = (mask or Mask()).to_c()
+    return int(lib.attn_fwd_kv_splits(ctypes.byref(_problem(q, k)), ctypes.byref(m), int(kv_splits)))
 
 
 def attn_bwd_workspace_bytes(q: torch.Tensor, k: torch.Tensor, mask: Optional[Mask] = None) -> int:
@@ -171,8 +185,12 @@ def attn_bwd_workspace_bytes(q: torch.Tensor, k: torch.Tensor, mask: Optional[Ma
 
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Optional[Mask] = None,
              scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
-             lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None):
-    """Forward: returns (O, LSE). O has q's dtype; LSE is float32 [batch, heads_q, seq_q]."""
+             lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None,
+             kv_splits: int = 0):
+    """Forward: returns (O, LSE). O has q's dtype; LSE is float32 [batch, heads_q, seq_q].
+
+    kv_splits: 0 lets the library choose a split of each item's key range, 1 never splits,
+    n > 1 forces n splits (attn_fwd_ex)."""
     lib = load_library()
     _check_tensors(q, k, v)
     mask = mask or Mask()
@@ -184,13 +202,14 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Optional[M
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
-    need = int(lib.attn_fwd_workspace_bytes(ctypes.byref(prob), ctypes.byref(cm)))
+    need = int(lib.attn_fwd_ex_workspace_bytes(ctypes.byref(prob), ctypes.byref(cm), int(kv_splits)))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = lib.attn_fwd(ctypes.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(cm),
-                      float(scale), out.data_ptr(), lse.data_ptr(), ws_ptr, ws_bytes, _stream_ptr(stream))
+    st = lib.attn_fwd_ex(ctypes.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(cm),
+                         float(scale), out.data_ptr(), lse.data_ptr(), ws_ptr, ws_bytes, int(kv_splits),
+                         _stream_ptr(stream))
     _raise(st)
     return out, lse
 

@@ -60,12 +60,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
   const int c = lane & 31, hh = lane >> 5;
   const int i16 = lane & 15, dsub = ((lane >> 4) & 1) * 16;
 
-  // ---- which tile of which (batch, head) ----
+  // ---- which tile of which (batch, head), and which part of its key range (split-KV) ----
+  const int split = (int)(blockIdx.x % (uint32_t)p.kv_splits);
+  const int item_idx = (int)(blockIdx.x / (uint32_t)p.kv_splits);
   Item it;
   if constexpr (MASK == MASK_NONE || MASK == MASK_CAUSAL) {
-    it = closed_form_item(blockIdx.x, p.batch, p.heads_q, p.heads_kv, p.n_qtiles, MASK == MASK_CAUSAL);
+    it = closed_form_item(item_idx, p.batch, p.heads_q, p.heads_kv, p.n_qtiles, MASK == MASK_CAUSAL);
   } else {
-    it = decode_item(p.items[blockIdx.x], p.heads_q, p.n_qtiles);
+    it = decode_item(p.items[item_idx], p.heads_q, p.n_qtiles);
   }
   const int b = it.b, h = it.h, kvh = h / p.group;
   const int q0 = it.t * BM;
@@ -288,13 +290,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
     n_free = p.seq_k / BN;
   }
   n_free = min(n_free, n_tiles);
+  // split-KV: this workgroup visits tiles [t0, t1) of the item's list, an equal share of it
+  int t0 = 0, t1 = n_tiles;
+  if (p.kv_splits > 1) {
+    const int chunk = (n_tiles + p.kv_splits - 1) / p.kv_splits;
+    t0 = min(split * chunk, n_tiles);
+    t1 = min(t0 + chunk, n_tiles);
+  }
+  const int t_free = min(max(n_free, t0), t1);
 
   auto step = [&](auto stage_tag, auto masked_tag, int j) __attribute__((always_inline)) {
     constexpr int ST = decltype(stage_tag)::value;
     constexpr bool MASKED = decltype(masked_tag)::value;
     wait_vmem();
     __syncthreads();  // tile j is in LDS; every wave is done with the stage tile j+1 will overwrite
-    if (j + 1 < n_tiles) issue_tile(std::integral_constant<int, 1 - ST>{}, tile_index(j + 1));
+    if (j + 1 < t1) issue_tile(std::integral_constant<int, 1 - ST>{}, tile_index(j + 1));
     const int k0 = tile_index(j) * BN;
     if constexpr (!MASKED) {
       bool active = true;
@@ -319,14 +329,38 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
     if (j < j1) step(std::integral_constant<int, 0>{}, masked_tag, j);
   };
 
-  if (n_tiles > 0) issue_tile(std::integral_constant<int, 0>{}, tile_index(0));
-  run(std::false_type{}, 0, n_free);
-  run(std::true_type{}, n_free, n_tiles);
+  // tile j lives in stage j % 2
+  if (t0 < t1) {
+    if (t0 & 1) issue_tile(std::integral_constant<int, 1>{}, tile_index(t0));
+    else issue_tile(std::integral_constant<int, 0>{}, tile_index(t0));
+  }
+  run(std::false_type{}, t0, t_free);
+  run(std::true_type{}, t_free, t1);
 
   // ---- epilogue: O = acc / l, LSE = ln 2 * (m + log2 l); empty rows give O = 0, LSE = -inf ----
   const float l = partner_sum(l_run + l_run2);
   const bool empty = !(l > 0.0f);
   const float inv = empty ? 0.0f : __builtin_amdgcn_rcpf(l);
+  if (p.kv_splits > 1) {
+    // partial result of this split: O over its keys in fp32 and its log2-sum-exp
+    if (my_q < p.seq_q) {
+      const size_t rows = (size_t)p.batch * p.heads_q * p.seq_q;
+      const size_t row = (size_t)(b * p.heads_q + h) * p.seq_q + my_q;
+      float* og = p.o_part + ((size_t)split * rows + row) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          f32x4 v4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v4[e] = acc[db][g4 * 4 + e] * inv;
+          *(f32x4*)(og + db * 32 + g4 * 8 + hh * 4) = v4;
+        }
+      }
+      if (hh == 0) p.lse_part[(size_t)split * rows + row] = empty ? -INFINITY : m_run + __builtin_amdgcn_logf(l);
+    }
+    return;
+  }
   if (my_q < p.seq_q) {
     bf16* og = (bf16*)p.o + q_off + (size_t)my_q * D;
 #pragma unroll
@@ -346,6 +380,37 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
   }
 }
 
+// ------------------------------------------------------------------------------------------------
+// Split-KV merge: the splits of one query row hold O_s (normalised over their keys) and
+// lse_s = log2 of their partial denominators (in the reference of the row maximum); the row's
+// result is LSE = log sum_s 2^lse_s and O = sum_s 2^(lse_s - LSE) O_s. D/4 lanes per row, 4 columns
+// each. A row no split saw gives O = 0, LSE = -inf.
+template <int D>
+__global__ __launch_bounds__(256) void fwd_merge_kernel(FwdParams p, int64_t rows) {
+  constexpr int LPR = D / 4;
+  const int64_t row = (int64_t)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
+  const int col = (threadIdx.x % LPR) * 4;
+  if (row >= rows) return;
+  float mx = -INFINITY;
+  for (int s = 0; s < p.kv_splits; ++s) mx = vmax(mx, p.lse_part[(size_t)s * rows + row]);
+  f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f};
+  float wsum = 0.0f;
+  if (mx != -INFINITY) {
+    for (int s = 0; s < p.kv_splits; ++s) {
+      const float w = fast_exp2(p.lse_part[(size_t)s * rows + row] - mx);
+      const f32x4 os = *(const f32x4*)(p.o_part + ((size_t)s * rows + row) * D + col);
+      o += w * os;
+      wsum += w;
+    }
+  }
+  const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+  bf16x4 v4;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v4[e] = (bf16)(o[e] * inv);
+  *(bf16x4*)((bf16*)p.o + row * D + col) = v4;
+  if (col == 0) p.lse[row] = wsum > 0.0f ? (mx + __builtin_amdgcn_logf(wsum)) * 0.69314718055994530942f : -INFINITY;
+}
+
 #ifndef ATTN_FWD_NW
 #define ATTN_FWD_NW 4
 #endif
@@ -355,7 +420,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
 
 template <int D, int NW, int MASK, int MINW>
 hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, MASK, MINW>), dim3(p.n_items), dim3(NW * 64), 0, stream, p);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, MASK, MINW>), dim3((uint32_t)p.n_items * (uint32_t)p.kv_splits),
+                     dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -379,6 +445,17 @@ int fwd_bf16_block_m(int head_dim, int mask) {
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int head_dim, int mask, hipStream_t stream) {
   return head_dim == 128 ? launch_mask<128>(p, mask, stream) : launch_mask<64>(p, mask, stream);
+}
+
+hipError_t launch_fwd_merge(const FwdParams& p, int head_dim, hipStream_t stream) {
+  const int64_t rows = (int64_t)p.batch * p.heads_q * p.seq_q;
+  const int rpb = 256 / (head_dim / 4);
+  const unsigned grid = (unsigned)((rows + rpb - 1) / rpb);
+  if (head_dim == 128)
+    hipLaunchKernelGGL(fwd_merge_kernel<128>, dim3(grid), dim3(256), 0, stream, p, rows);
+  else
+    hipLaunchKernelGGL(fwd_merge_kernel<64>, dim3(grid), dim3(256), 0, stream, p, rows);
+  return hipGetLastError();
 }
 
 }  // namespace attn

@@ -29,9 +29,11 @@ struct PlanParams {
 };
 
 hipError_t launch_plan(const PlanParams& p, hipStream_t stream);
+hipError_t launch_plan_pair(const PlanParams& a, const PlanParams& b, hipStream_t stream);
 
 int fwd_bf16_block_m(int head_dim, int mask);
 hipError_t launch_fwd_bf16(const FwdParams& p, int head_dim, int mask, hipStream_t stream);
+hipError_t launch_fwd_merge(const FwdParams& p, int head_dim, hipStream_t stream);
 
 int fwd_f32_block_m();
 hipError_t launch_fwd_f32(const FwdParams& p, int head_dim, int mask, hipStream_t stream);

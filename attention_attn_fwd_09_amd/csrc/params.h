@@ -26,6 +26,10 @@ struct FwdParams {
   int32_t nb_q, nb_k;           // BLOCK layout dims (64 x 64 tiles)
   float scale;                  // softmax scale
   float scale_log2;             // scale * log2(e)
+  int32_t kv_splits;            // workgroups sharing one item's key range (1 = no split)
+  float* o_part;                // kv_splits > 1: per-split O (normalised over the split), fp32
+                                //   [kv_splits][batch * heads_q * seq_q][head_dim]
+  float* lse_part;              // kv_splits > 1: per-split log2-sum-exp, fp32 [kv_splits][rows]
 };
 
 struct BwdParams {

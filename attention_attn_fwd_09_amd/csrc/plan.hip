@@ -145,7 +145,7 @@ __device__ int block_exclusive_scan(int v, int* wave_sums) {
   return wave_sums[wave] + incl - v;
 }
 
-__global__ __launch_bounds__(THREADS) void plan_kernel(PlanParams p) {
+__device__ __forceinline__ void plan_items(const PlanParams& p) {
   __shared__ int bucket[NBUCKET];
   __shared__ int wave_sums[THREADS / 64];
   __shared__ uint16_t cached[MAX_CACHED];
@@ -222,10 +222,22 @@ __global__ __launch_bounds__(THREADS) void plan_kernel(PlanParams p) {
   }
 }
 
+__global__ __launch_bounds__(THREADS) void plan_kernel(PlanParams p) { plan_items(p); }
+
+// Two independent item lists (the backward's dK/dV and dQ lists) in one launch, one workgroup each.
+__global__ __launch_bounds__(THREADS) void plan_pair_kernel(PlanParams a, PlanParams b) {
+  plan_items(blockIdx.x == 0 ? a : b);
+}
+
 }  // namespace
 
 hipError_t launch_plan(const PlanParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(THREADS), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_plan_pair(const PlanParams& a, const PlanParams& b, hipStream_t stream) {
+  hipLaunchKernelGGL(plan_pair_kernel, dim3(2), dim3(THREADS), 0, stream, a, b);
   return hipGetLastError();
 }
 

@@ -27,7 +27,7 @@ import time
 METRIC = "attention fwd/bwd TFLOP/s (bf16) + % of MFMA peak on 1 MI355X, seq 2048-8192"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-KERNEL_NAMES = {0: "plan", 1: "fwd", 2: "bwd_pre", 3: "bwd_dkdv", 4: "bwd_dq"}
+KERNEL_NAMES = {0: "plan", 1: "fwd", 2: "bwd_pre", 3: "bwd_dkdv", 4: "bwd_dq", 5: "fwd_merge"}
 
 
 def log(msg: str):
@@ -307,8 +307,26 @@ def cpu_baseline(w, inp, pairs_total):
             "seconds": round(secs, 2)}
 
 
+def time_calls(torch, fn, n=20, warm=5):
+    """Median, min and mean milliseconds of n calls of fn after warm untimed calls (one event pair
+    per call on the current stream)."""
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    return ms[len(ms) // 2], ms[0], sum(ms) / len(ms)
+
+
 def forward_all(lib, torch, dev, workloads, workload_inputs):
-    """Extra diagnostics on stderr: forward-only TFLOP/s of every measured workload."""
+    """Extra diagnostics on stderr: forward-only TFLOP/s of every measured workload (median of 20
+    calls after 5 warm-up calls; min and mean alongside), then split-KV against no split on shapes
+    with few work items."""
     for cfg, w in workloads.items():
         inp = workload_inputs(cfg)
         q, k, v = (inp[x].to(dev).contiguous() for x in ("q", "k", "v"))
@@ -317,20 +335,40 @@ def forward_all(lib, torch, dev, workloads, workload_inputs):
         o = torch.empty_like(q)
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
         ws = torch.empty(max(1, lib.attn_fwd_workspace_bytes(q, k, m)), dtype=torch.uint8, device=dev)
-        for _ in range(3):
-            lib.attn_fwd(q, k, v, mask=m, scale=inp["scale"], out=o, lse=lse, workspace=ws)
-        torch.cuda.synchronize()
-        n = 20
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(n):
-            lib.attn_fwd(q, k, v, mask=m, scale=inp["scale"], out=o, lse=lse, workspace=ws)
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / n
+        med, mn, mean = time_calls(torch, lambda: lib.attn_fwd(q, k, v, mask=m, scale=inp["scale"], out=o, lse=lse,
+                                                                 workspace=ws))
         fl = 4 * w.head_dim * visible_pairs(w, inp)
-        log(json.dumps({"workload": w.name, "fwd_ms": round(ms, 5), "fwd_tflops": round(fl / ms / 1e9, 2),
-                        "pct_peak": round(100 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2)}))
+        log(json.dumps({"workload": w.name, "fwd_ms": round(med, 5), "fwd_ms_min": round(mn, 5),
+                        "fwd_ms_mean": round(mean, 5), "fwd_tflops": round(fl / med / 1e9, 2),
+                        "pct_peak": round(100 * fl / med / 1e9 / PEAK_BF16_TFLOPS, 2)}))
+    split_kv_diag(lib, torch, dev)
+
+
+def split_kv_diag(lib, torch, dev):
+    """Forward TFLOP/s with the automatic split-KV choice and with no split, on two shapes whose
+    items leave most workgroup slots idle: few heads with long keys, and short query blocks
+    against long keys (decode-like)."""
+    from attention_attn_fwd_09_amd.inputs import Workload, make_inputs
+
+    shapes = (Workload("fwd_bf16_b1_h2_s16384_d128_none", "bf16", 1, 2, 2, 16384, 16384, 128, "none"),
+              Workload("fwd_bf16_b4_hq32_hkv8_sq128_sk32768_d128_none", "bf16", 4, 32, 8, 128, 32768, 128, "none"))
+    for i, w in enumerate(shapes):
+        inp = make_inputs(w, 7000 + i)
+        q, k, v = (inp[x].to(dev).contiguous() for x in ("q", "k", "v"))
+        m = lib.Mask()
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        line = {"workload": w.name}
+        fl = 4 * w.head_dim * w.batch * w.heads_q * w.seq_q * w.seq_k
+        for label, splits in (("auto", 0), ("nosplit", 1)):
+            ws = torch.empty(max(1, lib.attn_fwd_workspace_bytes(q, k, m, kv_splits=splits)), dtype=torch.uint8,
+                             device=dev)
+            med, mn, _ = time_calls(torch, lambda: lib.attn_fwd(q, k, v, mask=m, scale=inp["scale"], out=o, lse=lse,
+                                                                  workspace=ws, kv_splits=splits))
+            line[f"{label}_splits"] = lib.attn_fwd_kv_splits(q, k, m, splits)
+            line[f"{label}_ms"] = round(med, 5)
+            line[f"{label}_tflops"] = round(fl / med / 1e9, 2)
+        log(json.dumps(line))
 
 
 def main():

@@ -103,7 +103,8 @@ typedef struct {
   int32_t block_q, block_k;
 } attn_mask;
 
-/* Bytes of workspace attn_fwd needs for this problem and mask (0 if none). */
+/* Bytes of workspace attn_fwd needs for this problem and mask (0 if none). Equal to
+ * attn_fwd_ex_workspace_bytes(problem, mask, 0). */
 size_t attn_fwd_workspace_bytes(const attn_problem *problem, const attn_mask *mask);
 
 /*
@@ -117,6 +118,30 @@ size_t attn_fwd_workspace_bytes(const attn_problem *problem, const attn_mask *ma
 attn_status attn_fwd(const attn_problem *problem, const void *Q, const void *K, const void *V,
                      const attn_mask *mask, float scale, void *O, float *LSE,
                      void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Forward with a split of every work item's key range (split-KV), following the core split
+ * along the sequence direction of the fused multi-head attention operator write-up (zwxr.cn),
+ * section 4.2 (split by head first, then by sequence, to keep every core busy).
+ * kv_splits workgroups share the key tiles of one (batch, head, query tile) item in equal runs;
+ * each writes its partial O (normalised over its keys, fp32) and the log of its partial
+ * denominator to the workspace. A merge kernel then writes LSE = log sum_s exp(LSE_s) and
+ * O = sum_s exp(LSE_s - LSE) O_s. The result equals attn_fwd's up to rounding.
+ * kv_splits: 0 = automatic (split only when there are fewer items than the GPU has compute
+ * units, with at least 8 key tiles per split), 1 = never split, 2..32 = that many splits (at most one per
+ * 64-key tile). A value outside 0..32 returns ATTN_ERR_SHAPE; more than 1 with F32 returns
+ * ATTN_ERR_UNSUPPORTED. Other arguments and errors are as for attn_fwd; the workspace must hold
+ * attn_fwd_ex_workspace_bytes(problem, mask, kv_splits) bytes.
+ */
+attn_status attn_fwd_ex(const attn_problem *problem, const void *Q, const void *K, const void *V,
+                        const attn_mask *mask, float scale, void *O, float *LSE,
+                        void *workspace, size_t workspace_bytes, int32_t kv_splits, void *stream);
+
+/* Workspace bytes of attn_fwd_ex with this kv_splits (0 for an invalid problem). */
+size_t attn_fwd_ex_workspace_bytes(const attn_problem *problem, const attn_mask *mask, int32_t kv_splits);
+
+/* Number of splits attn_fwd_ex would use for this kv_splits (0 for an invalid problem). */
+int32_t attn_fwd_kv_splits(const attn_problem *problem, const attn_mask *mask, int32_t kv_splits);
 
 /* Bytes of workspace attn_bwd needs (the planner lists, D = rowsum(dO * O) and LSE * log2(e)). */
 size_t attn_bwd_workspace_bytes(const attn_problem *problem, const attn_mask *mask);
@@ -143,7 +168,8 @@ typedef enum {
   ATTN_KERNEL_BWD_PRE = 2,  /* backward preprocess, Delta = rowsum(dO * O) */
   ATTN_KERNEL_BWD_DKDV = 3, /* backward dK/dV pass */
   ATTN_KERNEL_BWD_DQ = 4,   /* backward dQ pass */
-  ATTN_KERNEL_CLASSES = 5
+  ATTN_KERNEL_FWD_MERGE = 5, /* split-KV merge of the forward */
+  ATTN_KERNEL_CLASSES = 6
 } attn_kernel_class;
 /*
  * While set for a class, each launch of that class records start_events[i] before it and

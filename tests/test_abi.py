@@ -37,7 +37,8 @@ def _declared_functions():
 def test_header_declares_expected_entry_points():
     names = _declared_functions()
     for n in ("attn_fwd", "attn_bwd", "attn_fwd_workspace_bytes", "attn_bwd_workspace_bytes", "attn_status_string",
-              "attn_version", "attn_set_timing_events"):
+              "attn_version", "attn_set_timing_events", "attn_fwd_ex", "attn_fwd_ex_workspace_bytes",
+              "attn_fwd_kv_splits"):
         assert n in names
 
 
@@ -190,7 +191,7 @@ def test_bwd_rejections():
 def test_timing_hook_argument_checks():
     lib = _lib()
     assert lib.attn_set_timing_events(-1, None, None, 0, None) == B.ATTN_ERR_SHAPE
-    assert lib.attn_set_timing_events(5, None, None, 0, None) == B.ATTN_ERR_SHAPE
+    assert lib.attn_set_timing_events(6, None, None, 0, None) == B.ATTN_ERR_SHAPE
     arr = (ctypes.c_void_p * 1)()
     assert lib.attn_set_timing_events(1, arr, arr, 1, None) == B.ATTN_ERR_NULL
     assert lib.attn_set_timing_events(1, None, None, 0, None) == B.ATTN_OK
@@ -203,3 +204,39 @@ def test_python_binding_rejects_noncontiguous_and_mixed_dtypes():
         B.attn_fwd(q.transpose(1, 2), q, q)
     with pytest.raises(TypeError):
         B.attn_fwd(q.to(torch.float16), q, q)
+
+
+def test_split_kv_arguments_and_choice():
+    lib = _lib()
+    ptr = _fwd_ok_ptrs()
+
+    def fwd_ex(p, m, splits, ws=None, wsb=0):
+        return lib.attn_fwd_ex(ctypes.byref(p), ptr["q"], ptr["k"], ptr["v"], ctypes.byref(m), 0.1, ptr["o"],
+                               ptr["lse"], ws, wsb, splits, None)
+
+    small = _problem(b=1, hq=2, hkv=1, sq=8192, sk=8192, d=128)
+    m = _mask()
+    assert fwd_ex(small, m, -1) == B.ATTN_ERR_SHAPE
+    assert fwd_ex(small, m, 33) == B.ATTN_ERR_SHAPE
+    assert fwd_ex(_problem(dtype=B.ATTN_F32), m, 2) == B.ATTN_ERR_UNSUPPORTED
+    # 128 items of 128 queries leave most workgroup slots idle: split, 8+ key tiles each
+    auto = lib.attn_fwd_kv_splits(ctypes.byref(small), ctypes.byref(m), 0)
+    assert 2 <= auto <= 32 and 128 // auto >= 8
+    assert lib.attn_fwd_kv_splits(ctypes.byref(small), ctypes.byref(m), 1) == 1
+    assert lib.attn_fwd_kv_splits(ctypes.byref(small), ctypes.byref(m), 7) == 7
+    # forced splits are capped at one per 64-key tile
+    short = _problem(b=1, hq=2, hkv=1, sq=150, sk=150, d=64)
+    assert lib.attn_fwd_kv_splits(ctypes.byref(short), ctypes.byref(m), 32) == 3
+    # many items: no split; fp32 never splits
+    big = _problem(b=4, hq=32, hkv=32, sq=4096, sk=4096, d=128)
+    assert lib.attn_fwd_kv_splits(ctypes.byref(big), ctypes.byref(m), 0) == 1
+    assert lib.attn_fwd_kv_splits(ctypes.byref(_problem(dtype=B.ATTN_F32)), ctypes.byref(m), 0) == 1
+    # the partial results live in the workspace: rows * (D + 1) fp32 per split
+    rows = 1 * 2 * 8192
+    need = lib.attn_fwd_ex_workspace_bytes(ctypes.byref(small), ctypes.byref(m), 4)
+    assert need >= 4 * rows * (128 + 1) * 4
+    assert lib.attn_fwd_ex_workspace_bytes(ctypes.byref(small), ctypes.byref(m), 1) == 0
+    assert lib.attn_fwd_workspace_bytes(ctypes.byref(small), ctypes.byref(m)) == \
+        lib.attn_fwd_ex_workspace_bytes(ctypes.byref(small), ctypes.byref(m), 0)
+    assert fwd_ex(small, m, 4) == B.ATTN_ERR_WORKSPACE
+    assert fwd_ex(small, m, 4, ws=ptr["ws"], wsb=need - 1) == B.ATTN_ERR_WORKSPACE
