@@ -32,6 +32,8 @@ ATTN_ERR_HIP = 9
 ATTN_F32 = 0
 ATTN_BF16 = 1
 
+ATTN_BWD_ATOMIC_DQ = 1  # attn_bwd_ex flag: single-pass backward with atomic fp32 dQ accumulation
+
 MASK_KINDS = {"none": 0, "causal": 1, "padding": 2, "block": 3}
 
 EXPORTED = ("attn_fwd", "attn_bwd", "attn_fwd_workspace_bytes", "attn_bwd_workspace_bytes",
@@ -87,6 +89,11 @@ def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
     lib.attn_fwd_kv_splits.restype = ctypes.c_int32
     lib.attn_bwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, pm, ctypes.c_float, vp, vp, vp, vp, sz, vp]
     lib.attn_bwd.restype = ctypes.c_int
+    lib.attn_bwd_ex.argtypes = [pp, vp, vp, vp, vp, vp, vp, pm, ctypes.c_float, vp, vp, vp, vp, sz, ctypes.c_int32,
+                                vp]
+    lib.attn_bwd_ex.restype = ctypes.c_int
+    lib.attn_bwd_ex_workspace_bytes.argtypes = [pp, pm, ctypes.c_int32]
+    lib.attn_bwd_ex_workspace_bytes.restype = sz
     lib.attn_status_string.argtypes = [ctypes.c_int]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -177,10 +184,10 @@ def attn_fwd_kv_splits(q: torch.Tensor, k: torch.Tensor, mask: Optional[Mask] = 
     return int(lib.attn_fwd_kv_splits(ctypes.byref(_problem(q, k)), ctypes.byref(m), int(kv_splits)))
 
 
-def attn_bwd_workspace_bytes(q: torch.Tensor, k: torch.Tensor, mask: Optional[Mask] = None) -> int:
+def attn_bwd_workspace_bytes(q: torch.Tensor, k: torch.Tensor, mask: Optional[Mask] = None, flags: int = 0) -> int:
     lib = load_library()
     m = (mask or Mask()).to_c()
-    return int(lib.attn_bwd_workspace_bytes(ctypes.byref(_problem(q, k)), ctypes.byref(m)))
+    return int(lib.attn_bwd_ex_workspace_bytes(ctypes.byref(_problem(q, k)), ctypes.byref(m), int(flags)))
 
 
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Optional[Mask] = None,
@@ -217,8 +224,12 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Optional[M
 def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, do: torch.Tensor,
              lse: torch.Tensor, mask: Optional[Mask] = None, scale: Optional[float] = None,
              dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
-             dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None):
-    """Backward: returns (dQ, dK, dV) in q's dtype."""
+             dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None,
+             flags: int = 0):
+    """Backward: returns (dQ, dK, dV) in q's dtype.
+
+    flags: 0 (two passes, deterministic) or ATTN_BWD_ATOMIC_DQ (single pass, dQ accumulated with
+    fp32 atomics; attn_bwd_ex)."""
     lib = load_library()
     _check_tensors(q, k, v, o, do, lse)
     mask = mask or Mask()
@@ -229,13 +240,13 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    need = int(lib.attn_bwd_workspace_bytes(ctypes.byref(prob), ctypes.byref(cm)))
+    need = int(lib.attn_bwd_ex_workspace_bytes(ctypes.byref(prob), ctypes.byref(cm), int(flags)))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = lib.attn_bwd(ctypes.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
-                      lse.data_ptr(), ctypes.byref(cm), float(scale), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                      ws_ptr, ws_bytes, _stream_ptr(stream))
+    st = lib.attn_bwd_ex(ctypes.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                         do.data_ptr(), lse.data_ptr(), ctypes.byref(cm), float(scale), dq.data_ptr(), dk.data_ptr(),
+                         dv.data_ptr(), ws_ptr, ws_bytes, int(flags), _stream_ptr(stream))
     _raise(st)
     return dq, dk, dv

@@ -132,10 +132,12 @@ attn_status check_splits(const attn_problem* p, const attn_mask* m, int32_t requ
 struct BwdSizes {
   int bq, bk, n_qt, n_kt;
   int64_t q_items, kv_items;
-  size_t delta_off, lse2_off, kv_off, q_off, total;
+  size_t delta_off, lse2_off, kv_off, q_off, dq_acc_off, total;
 };
 
-BwdSizes bwd_sizes(const attn_problem* p, const attn_mask* m) {
+// Two-pass layout: -Delta, LSE*log2(e), dK/dV items, dQ items. Single pass (ATTN_BWD_ATOMIC_DQ):
+// -Delta, LSE*log2(e), dK/dV items, then the fp32 dQ accumulator [B, Hq, Sq, D].
+BwdSizes bwd_sizes(const attn_problem* p, const attn_mask* m, int32_t flags = 0) {
   BwdSizes s;
   s.bq = bwd_block_q(p->head_dim, m->kind);
   s.bk = bwd_block_k(p->head_dim, m->kind);
@@ -147,7 +149,13 @@ BwdSizes bwd_sizes(const attn_problem* p, const attn_mask* m) {
   s.lse2_off = align_up((size_t)p->batch * p->heads_q * p->seq_q * 4);
   s.kv_off = s.lse2_off + align_up((size_t)p->batch * p->heads_q * p->seq_q * 4);
   s.q_off = s.kv_off + align_up((size_t)s.kv_items * 4);
-  s.total = s.q_off + align_up((size_t)s.q_items * 4);
+  if (flags & ATTN_BWD_ATOMIC_DQ) {
+    s.dq_acc_off = s.q_off;
+    s.total = s.dq_acc_off + align_up((size_t)p->batch * p->heads_q * p->seq_q * p->head_dim * 4);
+  } else {
+    s.dq_acc_off = 0;
+    s.total = s.q_off + align_up((size_t)s.q_items * 4);
+  }
   return s;
 }
 
@@ -330,17 +338,27 @@ attn_status attn_fwd_ex(const attn_problem* problem, const void* Q, const void* 
   return hip_status(timed(ATTN_KERNEL_FWD_MERGE, s, [&] { return launch_fwd_merge(fp, p->head_dim, s); }));
 }
 
-size_t attn_bwd_workspace_bytes(const attn_problem* problem, const attn_mask* mask) {
+size_t attn_bwd_ex_workspace_bytes(const attn_problem* problem, const attn_mask* mask, int32_t flags) {
   if (problem == nullptr) return 0;
   const attn_mask* m = mask ? mask : &kNoMask;
   if (check_problem(problem, m, 1.0f) != ATTN_OK) return 0;
-  if (problem->dtype != ATTN_BF16) return 0;
-  return bwd_sizes(problem, m).total;
+  if (problem->dtype != ATTN_BF16 || (flags & ~ATTN_BWD_ATOMIC_DQ) != 0) return 0;
+  return bwd_sizes(problem, m, flags).total;
+}
+
+size_t attn_bwd_workspace_bytes(const attn_problem* problem, const attn_mask* mask) {
+  return attn_bwd_ex_workspace_bytes(problem, mask, 0);
 }
 
 attn_status attn_bwd(const attn_problem* problem, const void* Q, const void* K, const void* V, const void* O,
                      const void* dO, const float* LSE, const attn_mask* mask, float scale, void* dQ, void* dK,
                      void* dV, void* workspace, size_t workspace_bytes, void* stream) {
+  return attn_bwd_ex(problem, Q, K, V, O, dO, LSE, mask, scale, dQ, dK, dV, workspace, workspace_bytes, 0, stream);
+}
+
+attn_status attn_bwd_ex(const attn_problem* problem, const void* Q, const void* K, const void* V, const void* O,
+                        const void* dO, const float* LSE, const attn_mask* mask, float scale, void* dQ, void* dK,
+                        void* dV, void* workspace, size_t workspace_bytes, int32_t flags, void* stream) {
   if (problem == nullptr || Q == nullptr || K == nullptr || V == nullptr || O == nullptr || dO == nullptr ||
       LSE == nullptr || dQ == nullptr || dK == nullptr || dV == nullptr)
     return ATTN_ERR_NULL;
@@ -348,6 +366,8 @@ attn_status attn_bwd(const attn_problem* problem, const void* Q, const void* K, 
   const attn_problem* p = problem;
   attn_status st = check_problem(p, m, scale);
   if (st != ATTN_OK) return st;
+  if ((flags & ~ATTN_BWD_ATOMIC_DQ) != 0) return ATTN_ERR_SHAPE;
+  const bool atomic_dq = (flags & ATTN_BWD_ATOMIC_DQ) != 0;
   if (p->dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
   if (m->kind == ATTN_MASK_BLOCK) {
     // the dK/dV pass lists (query head, layout row) pairs of its column: 6 + 10 bits each
@@ -356,7 +376,7 @@ attn_status attn_bwd(const attn_problem* problem, const void* Q, const void* K, 
   }
   for (const void* ptr : {Q, K, V, O, dO, (const void*)LSE, (const void*)dQ, (const void*)dK, (const void*)dV})
     if (!aligned16(ptr)) return ATTN_ERR_ALIGN;
-  const BwdSizes bs = bwd_sizes(p, m);
+  const BwdSizes bs = bwd_sizes(p, m, flags);
   if (workspace == nullptr || workspace_bytes < bs.total) return ATTN_ERR_WORKSPACE;
   if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
 
@@ -403,6 +423,7 @@ attn_status attn_bwd(const attn_problem* problem, const void* Q, const void* K, 
   bp.nb_q = ceil_div(p->seq_q, 64); bp.nb_k = ceil_div(p->seq_k, 64);
   bp.scale = scale;
   bp.scale_log2 = (scale > 0.0f ? scale : 1e-30f) * 1.4426950408889634f;
+  if (atomic_dq) bp.dq_acc = (float*)(ws + bs.dq_acc_off);
 
   PlanParams pp;
   std::memset(&pp, 0, sizeof(pp));
@@ -415,7 +436,10 @@ attn_status attn_bwd(const attn_problem* problem, const void* Q, const void* K, 
   pk.n_items = (int32_t)bs.kv_items; pk.items = (uint32_t*)(ws + bs.kv_off);
   pq.mode = PLAN_FWD_Q; pq.heads = p->heads_q; pq.n_tiles = bs.n_qt; pq.tile = bs.bq;
   pq.n_items = (int32_t)bs.q_items; pq.items = (uint32_t*)(ws + bs.q_off);
-  st = hip_status(timed(ATTN_KERNEL_PLAN, s, [&] { return launch_plan_pair(pk, pq, s); }));
+  if (atomic_dq)
+    st = hip_status(timed(ATTN_KERNEL_PLAN, s, [&] { return launch_plan(pk, s); }));
+  else
+    st = hip_status(timed(ATTN_KERNEL_PLAN, s, [&] { return launch_plan_pair(pk, pq, s); }));
   if (st != ATTN_OK) return st;
 
   st = hip_status(timed(ATTN_KERNEL_BWD_PRE, s, [&] { return launch_bwd_preprocess(bp, p->head_dim, s); }));
@@ -423,6 +447,8 @@ attn_status attn_bwd(const attn_problem* problem, const void* Q, const void* K, 
   st = hip_status(timed(ATTN_KERNEL_BWD_DKDV, s,
                         [&] { return launch_bwd_dkdv(bp, p->head_dim, m->kind, (int)bs.kv_items, s); }));
   if (st != ATTN_OK) return st;
+  if (atomic_dq)
+    return hip_status(timed(ATTN_KERNEL_BWD_DQ_CONVERT, s, [&] { return launch_bwd_dq_convert(bp, p->head_dim, s); }));
   return hip_status(
       timed(ATTN_KERNEL_BWD_DQ, s, [&] { return launch_bwd_dq(bp, p->head_dim, m->kind, (int)bs.q_items, s); }));
 }

@@ -55,6 +55,12 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int64_t rows)
   }
 #pragma unroll
   for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
+  if (p.dq_acc != nullptr && row < rows) {
+    // single-pass mode: this row's slice of the dQ accumulator starts at zero
+    float* z = p.dq_acc + row * D + sub * 8;
+    *(f32x4*)z = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    *(f32x4*)(z + 4) = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
   if (row < rows && sub == 0) {
     p.delta[row] = -acc;
     p.lse2[row] = lse_to_log2(p.lse[row]);
@@ -71,23 +77,31 @@ struct KvLds {
   static constexpr int MAX_STEPS = 4096;    // listed (query head, layout row) pairs for block masks
 };
 
-template <int D, int NW, int MASK>
+// ATOMIC_DQ: the single-pass variant (the write-conflict option of the Xingchen-Cup report,
+// section 03): the same pass also adds every step's dQ_i contribution, dS K_j, to an fp32
+// accumulator with hardware float atomics; a convert kernel scales and rounds it afterwards.
+template <int D, int NW, int MASK, bool ATOMIC_DQ = false>
 __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int BK = NW * 32;   // keys per workgroup
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
   constexpr int RB = D * 2;
   using L = KvLds<D>;
+  // the single-pass variant copies only the 256 bytes of row statistics (lanes 0-15), which
+  // leaves room for its per-wave dS tiles at two workgroups per CU
+  constexpr int STATS = ATOMIC_DQ ? 256 : L::STATS;
   __shared__ __attribute__((aligned(16))) char q_st0[L::TILE];
   __shared__ __attribute__((aligned(16))) char o_st0[L::TILE];   // dO
   __shared__ __attribute__((aligned(16))) char q_st1[L::TILE];
   __shared__ __attribute__((aligned(16))) char o_st1[L::TILE];
-  __shared__ __attribute__((aligned(16))) char l_st0[L::STATS];  // LSE * log2(e)
-  __shared__ __attribute__((aligned(16))) char d_st0[L::STATS];  // -Delta
-  __shared__ __attribute__((aligned(16))) char l_st1[L::STATS];
-  __shared__ __attribute__((aligned(16))) char d_st1[L::STATS];
+  __shared__ __attribute__((aligned(16))) char l_st0[STATS];  // LSE * log2(e)
+  __shared__ __attribute__((aligned(16))) char d_st0[STATS];  // -Delta
+  __shared__ __attribute__((aligned(16))) char l_st1[STATS];
+  __shared__ __attribute__((aligned(16))) char d_st1[STATS];
   __shared__ uint16_t list[MASK == MASK_BLOCK ? L::MAX_STEPS : 1];
   __shared__ int list_count;
+  // single-pass variant: each wave's dS of one 32-query block, [key][query] bf16, 64-byte rows
+  __shared__ __attribute__((aligned(16))) char ds_t[ATOMIC_DQ ? NW * 2048 : 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -197,9 +211,12 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdParams p) {
       const __amdgpu_buffer_rsrc_t rl = make_rsrc(p.lse2 + r_off, (uint32_t)p.seq_q * 4);
       const __amdgpu_buffer_rsrc_t rd = make_rsrc(p.delta + r_off, (uint32_t)p.seq_q * 4);
       // lanes 0-15 fetch the 64 row values; the others point past the buffer and write zeros
+      // (the single-pass variant leaves them inactive, so only 256 bytes are written)
       const uint32_t off = lane < 16 ? (uint32_t)(qt * BQ + lane * 4) * 4 : 0x80000000u;
-      buffer_to_lds16(rl, ST == 0 ? l_st0 : l_st1, off);
-      buffer_to_lds16(rd, ST == 0 ? d_st0 : d_st1, off);
+      if (!ATOMIC_DQ || lane < 16) {
+        buffer_to_lds16(rl, ST == 0 ? l_st0 : l_st1, off);
+        buffer_to_lds16(rd, ST == 0 ? d_st0 : d_st1, off);
+      }
     }
   };
 
@@ -360,6 +377,116 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdParams p) {
     __builtin_amdgcn_sched_group_barrier(0x008, 4 * DB, 0);
   };
 
+  // ---- single-pass variant: K fragments along the key direction (B operand of dQ = dS K) ----
+  // lane (c, hh) holds K[kw0 + kk*16 + hh*8 + e][db*32 + c], e = 0..7, read once per workgroup
+  bf16x8 kcol[ATOMIC_DQ ? DB : 1][2];
+  if constexpr (ATOMIC_DQ) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t off = ((uint32_t)(kw0 + kk * 16 + hh * 8 + e) * D + (uint32_t)(db * 32 + c)) * 2;
+          kcol[db][kk][e] = __builtin_bit_cast(bf16, __builtin_amdgcn_raw_buffer_load_b16(rk, off, 0, 0));
+        }
+      }
+    }
+  }
+
+  // One step of the single-pass variant, one 32-query block at a time: the two-pass body's
+  // products, then dQ_i += dS K_j for this wave's 32 keys, added to the fp32 accumulator.
+  auto body_atomic = [&](auto stage_tag, auto masked_tag, int q0, int hq) __attribute__((always_inline)) {
+    constexpr int ST = decltype(stage_tag)::value;
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const char* ql = ST == 0 ? q_st0 : q_st1;
+    const char* dol = ST == 0 ? o_st0 : o_st1;
+    const float* lse_l = (const float*)(ST == 0 ? l_st0 : l_st1);
+    const float* del_l = (const float*)(ST == 0 ? d_st0 : d_st1);
+    char* dsl = ds_t + wave * 2048;
+    float* dqa = p.dq_acc + ((size_t)(b * p.heads_q + hq) * p.seq_q) * D;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int qbase = qb * 32 + hh * 16;
+      f32x16 sc = f32x16{}, dp;
+      f32x4 lse4[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        lse4[r] = *(const f32x4*)(lse_l + qbase + 4 * r);
+        const f32x4 d4 = *(const f32x4*)(del_l + qbase + 4 * r);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dp[4 * r + e] = d4[e];
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 qa = *(const bf16x8*)(ql + roff[ks] + qb * 32 * RB);
+        const bf16x8 oa = *(const bf16x8*)(dol + roff[ks] + qb * 32 * RB);
+        sc = mfma32(qa, kf[ks], sc);
+        dp = mfma32(oa, vf[ks], dp);
+      }
+      bf16x8 pb[2], dsb[2];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float pv = fast_exp2(fmaf(sc[i], cs, -lse4[i >> 2][i & 3]));
+        if constexpr (MASKED) {
+          const int q = q0 + qbase + i;
+          bool vis = q < q_len && my_k < kv_len;
+          if constexpr (MASK == MASK_CAUSAL) vis = vis && my_k <= q;
+          pv = vis ? pv : 0.0f;
+        }
+        pb[i >> 3][i & 7] = (bf16)pv;
+        dsb[i >> 3][i & 7] = (bf16)(pv * dp[i]);
+      }
+      // dV += P^T dO, dK += dS^T Q
+#pragma unroll
+      for (int hc = 0; hc < 2; ++hc) {
+        const int rows = (qb * 32 + hc * 8) * RB;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const i16x4 olo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, dol + toff[db][0] + rows));
+          const i16x4 ohi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, dol + toff[db][1] + rows));
+          const i16x4 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, ql + toff[db][0] + rows));
+          const i16x4 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, ql + toff[db][1] + rows));
+          dv[db] = mfma32(pb[hc], __builtin_bit_cast(bf16x8, __builtin_shufflevector(olo, ohi, 0, 1, 2, 3, 4, 5, 6, 7)), dv[db]);
+          dk[db] = mfma32(dsb[hc], __builtin_bit_cast(bf16x8, __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7)), dk[db]);
+        }
+      }
+      // dS to this wave's LDS tile as [key][query] (lane (c, hh) holds key c, queries hh*16 + 0..15)
+      *(bf16x8*)(dsl + c * 64 + (hh * 16) * 2) = dsb[0];
+      *(bf16x8*)(dsl + c * 64 + (hh * 16 + 8) * 2) = dsb[1];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // A operand of dQ = dS K (rows = queries): lane l gets query l % 32 and keys kk*16 + (l/32)*8 + 0..7,
+      // transposed reads of the [key][query] tile (16-lane group: query half (l/16)&1, key half l/32)
+      bf16x8 dsa[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int row = kk * 16 + hh * 8 + (i16 >> 2);
+        const int col = dsub + 4 * (i16 & 3);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, dsl + row * 64 + col * 2));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, dsl + (row + 4) * 64 + col * 2));
+        dsa[kk] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+      // the tile is rewritten by the next block: its reads complete before those writes
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // dQ rows q0 + qb*32 + (i/4)*8 + hh*4 + i%4, column db*32 + c: 32 consecutive floats per row
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        f32x16 part = f32x16{};
+        part = mfma32(dsa[0], kcol[db][0], part);
+        part = mfma32(dsa[1], kcol[db][1], part);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int q = q0 + qb * 32 + (i >> 2) * 8 + hh * 4 + (i & 3);
+          if (q < p.seq_q) unsafeAtomicAdd(dqa + (size_t)q * D + db * 32 + c, part[i]);
+        }
+      }
+    }
+  };
+
   auto step = [&](auto stage_tag, auto masked_tag, int s) __attribute__((always_inline)) {
     constexpr int ST = decltype(stage_tag)::value;
     constexpr bool MASKED = decltype(masked_tag)::value;
@@ -369,13 +496,17 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdParams p) {
     int g, qt;
     step_at(s, g, qt);
     const int q0 = qt * BQ;
+    auto run_body = [&]() __attribute__((always_inline)) {
+      if constexpr (ATOMIC_DQ) body_atomic(stage_tag, masked_tag, q0, kvh * p.group + g);
+      else body(stage_tag, masked_tag, q0);
+    };
     if constexpr (!MASKED) {
-      body(stage_tag, masked_tag, q0);
+      run_body();
     } else {
       bool active = kw0 < kv_len;
       if constexpr (MASK == MASK_CAUSAL) active = active && kw0 <= q0 + BQ - 1;
       if constexpr (MASK == MASK_PADDING) active = active && q0 < q_len;
-      if (active) body(stage_tag, masked_tag, q0);
+      if (active) run_body();
     }
   };
   auto run = [&](auto masked_tag, int s0, int s1) __attribute__((always_inline)) {
@@ -650,9 +781,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
 }
 
 // ------------------------------------------------------------------------------------------------
-template <int D, int NW, int MASK>
+template <int D, int NW, int MASK, bool ATOMIC_DQ = false>
 hipError_t launch_dkdv_one(const BwdParams& p, int n_items, hipStream_t s) {
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, MASK>), dim3(n_items), dim3(NW * 64), 0, s, p);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, MASK, ATOMIC_DQ>), dim3(n_items), dim3(NW * 64), 0, s, p);
   return hipGetLastError();
 }
 
@@ -664,12 +795,34 @@ hipError_t launch_dq_one(const BwdParams& p, int n_items, hipStream_t s) {
 
 template <int D>
 hipError_t dkdv_mask(const BwdParams& p, int mask, int n_items, hipStream_t s) {
+  if (p.dq_acc != nullptr) {
+    switch (mask) {
+      case MASK_NONE: return launch_dkdv_one<D, 4, MASK_NONE, true>(p, n_items, s);
+      case MASK_CAUSAL: return launch_dkdv_one<D, 4, MASK_CAUSAL, true>(p, n_items, s);
+      case MASK_PADDING: return launch_dkdv_one<D, 4, MASK_PADDING, true>(p, n_items, s);
+      default: return launch_dkdv_one<D, 2, MASK_BLOCK, true>(p, n_items, s);
+    }
+  }
   switch (mask) {
     case MASK_NONE: return launch_dkdv_one<D, 4, MASK_NONE>(p, n_items, s);
     case MASK_CAUSAL: return launch_dkdv_one<D, 4, MASK_CAUSAL>(p, n_items, s);
     case MASK_PADDING: return launch_dkdv_one<D, 4, MASK_PADDING>(p, n_items, s);
     default: return launch_dkdv_one<D, 2, MASK_BLOCK>(p, n_items, s);
   }
+}
+
+// Single-pass mode: dQ = scale * (accumulated dS K), rounded to bf16; D/4 lanes per row.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dq_convert_kernel(BwdParams p, int64_t rows) {
+  constexpr int LPR = D / 4;
+  const int64_t row = (int64_t)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
+  const int col = (threadIdx.x % LPR) * 4;
+  if (row >= rows) return;
+  const f32x4 a = *(const f32x4*)(p.dq_acc + row * D + col);
+  bf16x4 v4;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v4[e] = (bf16)(a[e] * p.scale);
+  *(bf16x4*)((bf16*)p.dq + row * D + col) = v4;
 }
 
 template <int D>
@@ -708,6 +861,17 @@ hipError_t launch_bwd_dkdv(const BwdParams& p, int head_dim, int mask, int n_ite
 
 hipError_t launch_bwd_dq(const BwdParams& p, int head_dim, int mask, int n_items, hipStream_t s) {
   return head_dim == 128 ? dq_mask<128>(p, mask, n_items, s) : dq_mask<64>(p, mask, n_items, s);
+}
+
+hipError_t launch_bwd_dq_convert(const BwdParams& p, int head_dim, hipStream_t s) {
+  const int64_t rows = (int64_t)p.batch * p.heads_q * p.seq_q;
+  const int rpb = 256 / (head_dim / 4);
+  const unsigned grid = (unsigned)((rows + rpb - 1) / rpb);
+  if (head_dim == 128)
+    hipLaunchKernelGGL(bwd_dq_convert_kernel<128>, dim3(grid), dim3(256), 0, s, p, rows);
+  else
+    hipLaunchKernelGGL(bwd_dq_convert_kernel<64>, dim3(grid), dim3(256), 0, s, p, rows);
+  return hipGetLastError();
 }
 
 }  // namespace attn

@@ -44,6 +44,7 @@ int bwd_block_k(int head_dim, int mask);
 int bwd_max_steps();  // (query head, query tile) pairs one dK/dV workgroup can list for a block mask
 hipError_t launch_bwd_preprocess(const BwdParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdParams& p, int head_dim, int mask, int n_items, hipStream_t stream);
+hipError_t launch_bwd_dq_convert(const BwdParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdParams& p, int head_dim, int mask, int n_items, hipStream_t stream);
 
 }  // namespace attn

@@ -44,6 +44,8 @@ struct BwdParams {
   void* dv;
   float* delta;                 // workspace: -rowsum(dO * O) (negated Delta), fp32 [B, Hq, Sq]
   float* lse2;                  // workspace: LSE * log2(e), +inf for empty rows, fp32 [B, Hq, Sq]
+  float* dq_acc;                // single-pass mode: dQ / scale accumulated with fp32 atomics,
+                                //   [B, Hq, Sq, D]; zeroed by the preprocess; null otherwise
   const int32_t* lengths;
   const uint8_t* layout;
   int64_t layout_stride_b, layout_stride_h;

@@ -27,7 +27,7 @@ import time
 METRIC = "attention fwd/bwd TFLOP/s (bf16) + % of MFMA peak on 1 MI355X, seq 2048-8192"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-KERNEL_NAMES = {0: "plan", 1: "fwd", 2: "bwd_pre", 3: "bwd_dkdv", 4: "bwd_dq", 5: "fwd_merge"}
+KERNEL_NAMES = {0: "plan", 1: "fwd", 2: "bwd_pre", 3: "bwd_dkdv", 4: "bwd_dq", 5: "fwd_merge", 6: "bwd_dq_convert"}
 
 
 def log(msg: str):
@@ -342,6 +342,28 @@ def forward_all(lib, torch, dev, workloads, workload_inputs):
                         "fwd_ms_mean": round(mean, 5), "fwd_tflops": round(fl / med / 1e9, 2),
                         "pct_peak": round(100 * fl / med / 1e9 / PEAK_BF16_TFLOPS, 2)}))
     split_kv_diag(lib, torch, dev)
+    bwd_modes_diag(lib, torch, dev, workloads, workload_inputs)
+
+
+def bwd_modes_diag(lib, torch, dev, workloads, workload_inputs):
+    """Backward of the block-sparse workload: the two-pass default against the single pass with
+    atomic dQ accumulation (10*D algorithmic flops per visible pair in both)."""
+    cfg = 5
+    w = workloads[cfg]
+    inp = workload_inputs(cfg, with_do=True)
+    q, k, v, do = (inp[x].to(dev).contiguous() for x in ("q", "k", "v", "do"))
+    m = lib.Mask(kind="block", layout=inp["layout"].to(dev).contiguous())
+    o, lse = lib.attn_fwd(q, k, v, mask=m, scale=inp["scale"])
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    fl = 10 * w.head_dim * visible_pairs(w, inp)
+    line = {"workload": w.name + "_bwd"}
+    for label, flags in (("two_pass", 0), ("single_pass_atomic_dq", lib.ATTN_BWD_ATOMIC_DQ)):
+        ws = torch.empty(max(1, lib.attn_bwd_workspace_bytes(q, k, m, flags=flags)), dtype=torch.uint8, device=dev)
+        med, mn, _ = time_calls(torch, lambda: lib.attn_bwd(q, k, v, o, do, lse, mask=m, scale=inp["scale"], dq=dq,
+                                                             dk=dk, dv=dv, workspace=ws, flags=flags))
+        line[f"{label}_ms"] = round(med, 5)
+        line[f"{label}_tflops"] = round(fl / med / 1e9, 2)
+    log(json.dumps(line))
 
 
 def split_kv_diag(lib, torch, dev):

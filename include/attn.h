@@ -143,7 +143,8 @@ size_t attn_fwd_ex_workspace_bytes(const attn_problem *problem, const attn_mask 
 /* Number of splits attn_fwd_ex would use for this kv_splits (0 for an invalid problem). */
 int32_t attn_fwd_kv_splits(const attn_problem *problem, const attn_mask *mask, int32_t kv_splits);
 
-/* Bytes of workspace attn_bwd needs (the planner lists, D = rowsum(dO * O) and LSE * log2(e)). */
+/* Bytes of workspace attn_bwd needs (the planner lists, D = rowsum(dO * O) and LSE * log2(e)).
+ * Equal to attn_bwd_ex_workspace_bytes(problem, mask, 0). */
 size_t attn_bwd_workspace_bytes(const attn_problem *problem, const attn_mask *mask);
 
 /*
@@ -160,6 +161,33 @@ attn_status attn_bwd(const attn_problem *problem, const void *Q, const void *K, 
                      float scale, void *dQ, void *dK, void *dV, void *workspace,
                      size_t workspace_bytes, void *stream);
 
+/* Flags of attn_bwd_ex. */
+enum {
+  /* Single pass: the report on the sparse FlashAttention backward (Xingchen-Cup, smzdm.com),
+   * section 03, names two ways to resolve the conflicting accumulation directions of the three
+   * gradients: two loops, or many cores adding into the same place with write conflicts resolved.
+   * attn_bwd takes the two loops (a dK/dV pass and a dQ pass, deterministic). With this flag the
+   * dK/dV pass also adds each block's dQ contribution (dS K) into an fp32 accumulator in the
+   * workspace with hardware float atomics, and a convert kernel writes dQ = scale * accumulator
+   * in bf16: no second recomputation of S and dP, but dQ depends on the order of the atomic
+   * additions (not bitwise reproducible from run to run; dK and dV still are). */
+  ATTN_BWD_ATOMIC_DQ = 1
+};
+
+/*
+ * Backward with options (flags: 0 or ATTN_BWD_ATOMIC_DQ). Arguments, outputs and errors as for
+ * attn_bwd; an unknown flag returns ATTN_ERR_SHAPE; the workspace must hold
+ * attn_bwd_ex_workspace_bytes(problem, mask, flags) bytes (with ATTN_BWD_ATOMIC_DQ it includes
+ * a float32 [batch, heads_q, seq_q, head_dim] accumulator).
+ */
+attn_status attn_bwd_ex(const attn_problem *problem, const void *Q, const void *K, const void *V,
+                        const void *O, const void *dO, const float *LSE, const attn_mask *mask,
+                        float scale, void *dQ, void *dK, void *dV, void *workspace,
+                        size_t workspace_bytes, int32_t flags, void *stream);
+
+/* Workspace bytes of attn_bwd_ex with these flags (0 for an invalid problem or flag). */
+size_t attn_bwd_ex_workspace_bytes(const attn_problem *problem, const attn_mask *mask, int32_t flags);
+
 /*
  * Kernel timing hook, for profiling tools. Kernel classes: */
 typedef enum {
@@ -169,7 +197,8 @@ typedef enum {
   ATTN_KERNEL_BWD_DKDV = 3, /* backward dK/dV pass */
   ATTN_KERNEL_BWD_DQ = 4,   /* backward dQ pass */
   ATTN_KERNEL_FWD_MERGE = 5, /* split-KV merge of the forward */
-  ATTN_KERNEL_CLASSES = 6
+  ATTN_KERNEL_BWD_DQ_CONVERT = 6, /* single-pass backward: dQ accumulator to bf16 */
+  ATTN_KERNEL_CLASSES = 7
 } attn_kernel_class;
 /*
  * While set for a class, each launch of that class records start_events[i] before it and

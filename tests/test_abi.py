@@ -191,7 +191,7 @@ def test_bwd_rejections():
 def test_timing_hook_argument_checks():
     lib = _lib()
     assert lib.attn_set_timing_events(-1, None, None, 0, None) == B.ATTN_ERR_SHAPE
-    assert lib.attn_set_timing_events(6, None, None, 0, None) == B.ATTN_ERR_SHAPE
+    assert lib.attn_set_timing_events(7, None, None, 0, None) == B.ATTN_ERR_SHAPE
     arr = (ctypes.c_void_p * 1)()
     assert lib.attn_set_timing_events(1, arr, arr, 1, None) == B.ATTN_ERR_NULL
     assert lib.attn_set_timing_events(1, None, None, 0, None) == B.ATTN_OK
@@ -240,3 +240,24 @@ def test_split_kv_arguments_and_choice():
         lib.attn_fwd_ex_workspace_bytes(ctypes.byref(small), ctypes.byref(m), 0)
     assert fwd_ex(small, m, 4) == B.ATTN_ERR_WORKSPACE
     assert fwd_ex(small, m, 4, ws=ptr["ws"], wsb=need - 1) == B.ATTN_ERR_WORKSPACE
+
+
+def test_single_pass_backward_arguments():
+    lib = _lib()
+    q, k, v, o, do, lse, dq, dk, dv, ws = _spaced(10)
+    p, m = _problem(b=2, hq=4, hkv=2, sq=300, sk=300, d=128), _mask()
+    two = lib.attn_bwd_ex_workspace_bytes(ctypes.byref(p), ctypes.byref(m), 0)
+    one = lib.attn_bwd_ex_workspace_bytes(ctypes.byref(p), ctypes.byref(m), B.ATTN_BWD_ATOMIC_DQ)
+    assert two == lib.attn_bwd_workspace_bytes(ctypes.byref(p), ctypes.byref(m))
+    # the single pass keeps an fp32 [B, Hq, Sq, D] dQ accumulator instead of the dQ item list
+    assert one >= 2 * 4 * 300 * 128 * 4
+    assert lib.attn_bwd_ex_workspace_bytes(ctypes.byref(p), ctypes.byref(m), 2) == 0
+
+    def call(flags, wsb):
+        return lib.attn_bwd_ex(ctypes.byref(p), q, k, v, o, do, lse, ctypes.byref(m), 0.1, dq, dk, dv, ws, wsb,
+                               flags, None)
+
+    assert call(2, 1 << 40) == B.ATTN_ERR_SHAPE
+    assert call(-1, 1 << 40) == B.ATTN_ERR_SHAPE
+    assert call(B.ATTN_BWD_ATOMIC_DQ, one - 1) == B.ATTN_ERR_WORKSPACE
+    assert call(B.ATTN_BWD_ATOMIC_DQ, two) == B.ATTN_ERR_WORKSPACE
