@@ -15,7 +15,9 @@ full score matrix materialised, one (batch, head) pair at a time:
 * page 2, section 1.2 and page 1 (smzdm.com), section 03: the unfused form
   materialises the [seq_len, seq_len] score matrix; this oracle does exactly
   that, in float64;
-* page 2, section 3.3: a mask entry of 0 sends the score to minus infinity.
+* page 2, section 3.3: a mask entry of 0 sends the score to minus infinity
+  (the generic element mask mask[i][j]; the structured kinds below are
+  special cases of it).
 * page 1, section 03: the backward produces the three gradients dQ, dK, dV.
   They are written in closed form below from the chain rule through the
   softmax (the pages name the gradients but print no formula).
@@ -31,7 +33,8 @@ Readings taken where the pages are silent (each is listed in the design doc):
   over its G query heads;
 * causal masks key j for query i when j > i (top-left aligned, square only);
   padding keeps (i, j) when i < L_b and j < L_b; a block layout keeps the
-  whole block_q x block_k tile where the layout byte is non-zero.
+  whole block_q x block_k tile where the layout byte is non-zero; a dense mask
+  keeps (i, j) where its byte is non-zero.
 
 Nothing here is blocked, fused or reordered beyond the definition: a numpy
 matmul is the only library primitive used.
@@ -59,13 +62,16 @@ __all__ = [
 class MaskSpec:
     """Description of a structured mask, in the oracle's own terms.
 
-    kind: "none", "causal", "padding" or "block".
+    kind: "none", "causal", "padding", "block" or "dense".
     lengths: padding only; int array [batch], the valid length of both the
         queries and the keys of each batch element.
     layout: block only; uint8/bool array, either [nb_q, nb_k] (shared by every
         batch element and head) or [batch, heads_q, nb_q, nb_k]. Non-zero means
         the tile is kept.
     block_q, block_k: block only; tile sizes in query rows and key columns.
+    dense: dense only; uint8/bool array, either [sq, sk] (shared by every batch
+        element and head) or [batch, heads_q, sq, sk]. Non-zero means query i
+        attends to key j.
     """
 
     kind: str = "none"
@@ -73,6 +79,7 @@ class MaskSpec:
     layout: Optional[np.ndarray] = None
     block_q: int = 64
     block_k: int = 64
+    dense: Optional[np.ndarray] = None
 
 
 def mask_matrix(spec: MaskSpec, b: int, h: int, sq: int, sk: int) -> np.ndarray:
@@ -98,6 +105,11 @@ def mask_matrix(spec: MaskSpec, b: int, h: int, sq: int, sk: int) -> np.ndarray:
         rows = np.minimum(np.arange(sq) // spec.block_q, keep.shape[0] - 1)
         cols = np.minimum(np.arange(sk) // spec.block_k, keep.shape[1] - 1)
         return keep[rows[:, None], cols[None, :]]
+    if spec.kind == "dense":
+        arr = np.asarray(spec.dense)
+        if arr.ndim == 4:
+            arr = arr[b, h]
+        return arr[:sq, :sk] != 0
     raise ValueError(f"unknown mask kind {spec.kind!r}")
 
 
@@ -228,5 +240,8 @@ def attention_bwd_head(q, k, v, do, mask: MaskSpec, scale: float, b: int, h: int
     if mask.kind == "block":
         lay = np.asarray(mask.layout)
         sub.layout = lay[b:b + 1, h:h + 1] if lay.ndim == 4 else lay
+    if mask.kind == "dense":
+        arr = np.asarray(mask.dense)
+        sub.dense = arr[b:b + 1, h:h + 1] if arr.ndim == 4 else arr
     dq, dk, dv = attention_bwd(q64, k64, v64, do64, sub, scale)
     return dq[0, 0], dk[0, 0], dv[0, 0]

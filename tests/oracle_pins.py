@@ -44,7 +44,7 @@ def _qkv(seed, b, hq, hkv, sq, sk, d, dv=None):
             r.standard_normal((b, hkv, sk, dv)))
 
 
-def _torch_mask(kind, b, hq, sq, sk, lengths=None, layout=None, bq=64, bk=64):
+def _torch_mask(kind, b, hq, sq, sk, lengths=None, layout=None, bq=64, bk=64, dense=None):
     """[b, hq, sq, sk] bool (True = attend), built with torch ops."""
     if kind == "none":
         return torch.ones(b, hq, sq, sk, dtype=torch.bool)
@@ -61,11 +61,17 @@ def _torch_mask(kind, b, hq, sq, sk, lengths=None, layout=None, bq=64, bk=64):
         if dense.dim() == 2:
             dense = dense.expand(b, hq, sq, sk)
         return dense
+    if kind == "dense":
+        m = torch.as_tensor(np.asarray(dense)) != 0
+        return m.expand(b, hq, sq, sk) if m.dim() == 2 else m
     raise ValueError(kind)
 
 
-def _spec(mod, kind, lengths=None, layout=None, bq=64, bk=64):
-    return mod.MaskSpec(kind=kind, lengths=lengths, layout=layout, block_q=bq, block_k=bk)
+def _spec(mod, kind, lengths=None, layout=None, bq=64, bk=64, dense=None):
+    spec = mod.MaskSpec(kind=kind, lengths=lengths, layout=layout, block_q=bq, block_k=bk)
+    if dense is not None:
+        spec.dense = dense
+    return spec
 
 
 def _sdpa(q, k, v, tmask, scale):
@@ -104,6 +110,16 @@ def _mask_cases(mod):
                   _torch_mask("block", b, hq, s, s, layout=lay4, bq=8, bk=8)))
     # non-square, no mask, key count not a multiple of anything
     cases.append(("none_rect", 1, 2, 1, 5, 23, 8, _spec(mod, "none"), _torch_mask("none", 1, 2, 5, 23)))
+    # the generic element mask: shared by every (b, h), with one fully masked query row ...
+    dense = (r.random((s, s)) < 0.5).astype(np.uint8)
+    dense[5, :] = 0
+    cases.append(("dense_shared", b, hq, hkv, s, s, d, _spec(mod, "dense", dense=dense),
+                  _torch_mask("dense", b, hq, s, s, dense=dense)))
+    # ... and one per (b, h), non-square, every row keeping at least one key
+    dense4 = (r.random((b, hq, 9, s)) < 0.4).astype(np.uint8)
+    dense4[..., 0] = 1
+    cases.append(("dense_per_head", b, hq, hkv, 9, s, d, _spec(mod, "dense", dense=dense4),
+                  _torch_mask("dense", b, hq, 9, s, dense=dense4)))
     return cases
 
 
