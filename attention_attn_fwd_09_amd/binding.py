@@ -34,7 +34,7 @@ ATTN_BF16 = 1
 
 ATTN_BWD_ATOMIC_DQ = 1  # attn_bwd_ex flag: single-pass backward with atomic fp32 dQ accumulation
 
-MASK_KINDS = {"none": 0, "causal": 1, "padding": 2, "block": 3}
+MASK_KINDS = {"none": 0, "causal": 1, "padding": 2, "block": 3, "dense": 4}
 
 EXPORTED = ("attn_fwd", "attn_bwd", "attn_fwd_workspace_bytes", "attn_bwd_workspace_bytes",
             "attn_status_string", "attn_version")
@@ -49,7 +49,8 @@ class AttnProblem(ctypes.Structure):
 class AttnMask(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("lengths", ctypes.c_void_p), ("block_layout", ctypes.c_void_p),
                 ("layout_stride_b", ctypes.c_int64), ("layout_stride_h", ctypes.c_int64),
-                ("block_q", ctypes.c_int32), ("block_k", ctypes.c_int32)]
+                ("block_q", ctypes.c_int32), ("block_k", ctypes.c_int32), ("dense", ctypes.c_void_p),
+                ("dense_stride_b", ctypes.c_int64), ("dense_stride_h", ctypes.c_int64)]
 
 
 class AttnError(RuntimeError):
@@ -108,16 +109,19 @@ def attn_status_string(status: int) -> str:
 
 @dataclass
 class Mask:
-    """Mask descriptor: kind in {"none", "causal", "padding", "block"}.
+    """Mask descriptor: kind in {"none", "causal", "padding", "block", "dense"}.
 
     lengths: int32 device tensor [batch] (padding). layout: uint8 device tensor, [nb_q, nb_k]
-    shared by all (b, h), or [batch, heads_q, nb_q, nb_k] (block, 64x64 tiles).
+    shared by all (b, h), or [batch, heads_q, nb_q, nb_k] (block, 64x64 tiles). dense: uint8 (or
+    bool) device tensor [seq_q, seq_k] shared by all (b, h), or [batch, heads_q, seq_q, seq_k];
+    non-zero keeps the pair (dense).
     """
 
     kind: str = "none"
     lengths: Optional[torch.Tensor] = None
     layout: Optional[torch.Tensor] = None
     block: int = 64
+    dense: Optional[torch.Tensor] = None
 
     def to_c(self) -> AttnMask:
         m = AttnMask()
@@ -130,6 +134,13 @@ class Mask:
             if self.layout.dim() == 4:
                 m.layout_stride_b = self.layout.stride(0)
                 m.layout_stride_h = self.layout.stride(1)
+        if self.dense is not None:
+            if self.dense.element_size() != 1 or not self.dense.is_contiguous():
+                raise ValueError("dense mask must be a contiguous uint8 or bool tensor")
+            m.dense = self.dense.data_ptr()
+            if self.dense.dim() == 4:
+                m.dense_stride_b = self.dense.stride(0)
+                m.dense_stride_h = self.dense.stride(1)
         return m
 
 

@@ -34,7 +34,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
 
-const attn_mask kNoMask = {ATTN_MASK_NONE, nullptr, nullptr, 0, 0, 64, 64};
+const attn_mask kNoMask = {ATTN_MASK_NONE, nullptr, nullptr, 0, 0, 64, 64, nullptr, 0, 0};
 
 // Checks shared by forward and backward. `mask` is never null here.
 attn_status check_problem(const attn_problem* p, const attn_mask* m, float scale) {
@@ -57,6 +57,11 @@ attn_status check_problem(const attn_problem* p, const attn_mask* m, float scale
       if (m->layout_stride_b < 0 || m->layout_stride_h < 0) return ATTN_ERR_MASK;
       if (ceil_div(p->seq_k, 64) > MAX_BLOCK_COLS) return ATTN_ERR_UNSUPPORTED;
       break;
+    case ATTN_MASK_DENSE:
+      if (m->dense == nullptr) return ATTN_ERR_MASK;
+      if (m->dense_stride_b < 0 || m->dense_stride_h < 0) return ATTN_ERR_MASK;
+      if (ceil_div(p->seq_k, 64) > MAX_BLOCK_COLS) return ATTN_ERR_UNSUPPORTED;
+      break;
     default: return ATTN_ERR_MASK;
   }
   if (p->head_dim != 64 && p->head_dim != 128) return ATTN_ERR_UNSUPPORTED;
@@ -73,12 +78,72 @@ int64_t layout_bytes(const attn_problem* p, const attn_mask* m) {
   return (int64_t)(p->batch - 1) * m->layout_stride_b + (int64_t)(p->heads_q - 1) * m->layout_stride_h + nbq * nbk;
 }
 
+int64_t dense_bytes(const attn_problem* p, const attn_mask* m) {
+  return (int64_t)(p->batch - 1) * m->dense_stride_b + (int64_t)(p->heads_q - 1) * m->dense_stride_h +
+         (int64_t)p->seq_q * p->seq_k;
+}
+
+// Workspace of a packed dense mask (bf16 kernels): row bits, column bits (backward only) and the
+// derived 64x64 block layout, per distinct (batch element, query head) of the mask.
+struct DenseSizes {
+  int32_t batch_m, heads_m, row_words, col_words, nb_q, nb_k;
+  size_t rows_off, cols_off, layout_off, total;   // offsets from the region's start
+};
+
+DenseSizes dense_sizes(const attn_problem* p, const attn_mask* m, bool with_cols) {
+  DenseSizes z{};
+  if (m->kind != ATTN_MASK_DENSE || p->dtype != ATTN_BF16) return z;
+  z.batch_m = m->dense_stride_b != 0 ? p->batch : 1;
+  z.heads_m = m->dense_stride_h != 0 ? p->heads_q : 1;
+  z.row_words = ceil_div(p->seq_k, 32);
+  z.col_words = ceil_div(p->seq_q, 32);
+  z.nb_q = ceil_div(p->seq_q, 64);
+  z.nb_k = ceil_div(p->seq_k, 64);
+  const size_t n = (size_t)z.batch_m * z.heads_m;
+  z.rows_off = 0;
+  z.cols_off = align_up(n * p->seq_q * z.row_words * 4);
+  z.layout_off = z.cols_off + (with_cols ? align_up(n * p->seq_k * z.col_words * 4) : 0);
+  z.total = z.layout_off + align_up(n * z.nb_q * z.nb_k);
+  return z;
+}
+
+// Packs the caller's byte mask into the workspace region at `base` and returns the bit views.
+hipError_t pack_dense(const attn_problem* p, const attn_mask* m, const DenseSizes& z, char* base, bool with_cols,
+                      DenseBits* bits, const uint8_t** layout, int64_t* layout_sb, int64_t* layout_sh,
+                      hipStream_t s) {
+  DensePackParams dp;
+  std::memset(&dp, 0, sizeof(dp));
+  dp.mask = m->dense;
+  dp.stride_b = m->dense_stride_b;
+  dp.stride_h = m->dense_stride_h;
+  dp.batch_m = z.batch_m; dp.heads_m = z.heads_m;
+  dp.seq_q = p->seq_q; dp.seq_k = p->seq_k; dp.nb_q = z.nb_q; dp.nb_k = z.nb_k;
+  dp.row_bits = (uint32_t*)(base + z.rows_off);
+  dp.col_bits = with_cols ? (uint32_t*)(base + z.cols_off) : nullptr;
+  dp.row_words = z.row_words; dp.col_words = z.col_words;
+  dp.layout = (uint8_t*)(base + z.layout_off);
+  std::memset(bits, 0, sizeof(*bits));
+  bits->rows = dp.row_bits;
+  bits->cols = dp.col_bits;
+  bits->row_words = z.row_words;
+  bits->col_words = z.col_words;
+  bits->rows_stride_h = m->dense_stride_h != 0 ? (int64_t)p->seq_q * z.row_words : 0;
+  bits->rows_stride_b = m->dense_stride_b != 0 ? (int64_t)z.heads_m * p->seq_q * z.row_words : 0;
+  bits->cols_stride_h = m->dense_stride_h != 0 ? (int64_t)p->seq_k * z.col_words : 0;
+  bits->cols_stride_b = m->dense_stride_b != 0 ? (int64_t)z.heads_m * p->seq_k * z.col_words : 0;
+  *layout = dp.layout;
+  *layout_sh = m->dense_stride_h != 0 ? (int64_t)z.nb_q * z.nb_k : 0;
+  *layout_sb = m->dense_stride_b != 0 ? (int64_t)z.heads_m * z.nb_q * z.nb_k : 0;
+  return launch_dense_pack(dp, s);
+}
+
 int fwd_tile_m(const attn_problem* p, const attn_mask* m) {
   return p->dtype == ATTN_F32 ? fwd_f32_block_m() : fwd_bf16_block_m(p->head_dim, m->kind);
 }
 
 bool fwd_needs_plan(const attn_problem* p, const attn_mask* m) {
-  return p->dtype == ATTN_BF16 && (m->kind == ATTN_MASK_PADDING || m->kind == ATTN_MASK_BLOCK);
+  return p->dtype == ATTN_BF16 &&
+         (m->kind == ATTN_MASK_PADDING || m->kind == ATTN_MASK_BLOCK || m->kind == ATTN_MASK_DENSE);
 }
 
 int64_t fwd_items(const attn_problem* p, const attn_mask* m) {
@@ -107,13 +172,17 @@ int32_t fwd_splits(const attn_problem* p, const attn_mask* m, int32_t requested)
 }
 
 struct FwdSizes {
-  size_t plan_bytes, o_part_off, lse_part_off, total;
+  size_t plan_bytes, dense_off, o_part_off, lse_part_off, total;
+  DenseSizes dense;
 };
 
+// Forward workspace: planner items, packed dense mask, split-KV partials.
 FwdSizes fwd_sizes(const attn_problem* p, const attn_mask* m, int32_t splits) {
   FwdSizes z{};
   z.plan_bytes = fwd_needs_plan(p, m) ? align_up((size_t)fwd_items(p, m) * 4) : 0;
-  z.o_part_off = z.lse_part_off = z.total = z.plan_bytes;
+  z.dense = dense_sizes(p, m, false);
+  z.dense_off = z.plan_bytes;
+  z.o_part_off = z.lse_part_off = z.total = z.dense_off + z.dense.total;
   if (splits > 1) {
     const size_t rows = (size_t)p->batch * p->heads_q * p->seq_q;
     z.lse_part_off = z.o_part_off + align_up((size_t)splits * rows * p->head_dim * 4);
@@ -132,7 +201,8 @@ attn_status check_splits(const attn_problem* p, const attn_mask* m, int32_t requ
 struct BwdSizes {
   int bq, bk, n_qt, n_kt;
   int64_t q_items, kv_items;
-  size_t delta_off, lse2_off, kv_off, q_off, dq_acc_off, total;
+  size_t delta_off, lse2_off, kv_off, q_off, dq_acc_off, dense_off, total;
+  DenseSizes dense;
 };
 
 // Two-pass layout: -Delta, LSE*log2(e), dK/dV items, dQ items. Single pass (ATTN_BWD_ATOMIC_DQ):
@@ -156,6 +226,10 @@ BwdSizes bwd_sizes(const attn_problem* p, const attn_mask* m, int32_t flags = 0)
     s.dq_acc_off = 0;
     s.total = s.q_off + align_up((size_t)s.q_items * 4);
   }
+  // a dense mask's bits (rows and columns) and block layout follow
+  s.dense = dense_sizes(p, m, true);
+  s.dense_off = s.total;
+  s.total += s.dense.total;
   return s;
 }
 
@@ -198,7 +272,7 @@ const char* attn_status_string(attn_status s) {
     case ATTN_ERR_SHAPE: return "invalid sizes (dimension < 1, heads_q not a multiple of heads_kv, seq_q != seq_k for a causal mask, or scale not finite and >= 0)";
     case ATTN_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
     case ATTN_ERR_DTYPE: return "unknown dtype";
-    case ATTN_ERR_MASK: return "invalid mask descriptor (unknown kind, missing lengths or layout, block size other than 64, negative stride)";
+    case ATTN_ERR_MASK: return "invalid mask descriptor (unknown kind, missing lengths, layout or dense mask, block size other than 64, negative stride)";
     case ATTN_ERR_WORKSPACE: return "workspace too small or missing";
     case ATTN_ERR_ALIAS: return "an output overlaps an input or another output";
     case ATTN_ERR_UNSUPPORTED: return "valid but unsupported problem (head_dim must be 64 or 128; sizes beyond the 32-bit slice limit; backward needs bf16)";
@@ -207,7 +281,7 @@ const char* attn_status_string(attn_status s) {
   return "unknown status";
 }
 
-int32_t attn_version(void) { return 101; }
+int32_t attn_version(void) { return 102; }
 
 attn_status attn_set_timing_events(int32_t kernel_class, void* const* start_events, void* const* stop_events,
                                    int32_t capacity, int32_t* count) {
@@ -289,6 +363,10 @@ attn_status attn_fwd_ex(const attn_problem* problem, const void* Q, const void* 
     const Range rlay = range_of(m->block_layout, (size_t)layout_bytes(p, m));
     if (overlap(rlay, ro) || overlap(rlay, rl) || (need > 0 && overlap(rlay, rw))) return ATTN_ERR_ALIAS;
   }
+  if (m->kind == ATTN_MASK_DENSE) {
+    const Range rden = range_of(m->dense, (size_t)dense_bytes(p, m));
+    if (overlap(rden, ro) || overlap(rden, rl) || (need > 0 && overlap(rden, rw))) return ATTN_ERR_ALIAS;
+  }
 
   // ---- launch ----
   hipStream_t s = (hipStream_t)stream;
@@ -311,6 +389,9 @@ attn_status attn_fwd_ex(const attn_problem* problem, const void* Q, const void* 
   // kernels rely on scale*log2(e) > 0 (masked scores are -inf); scale 0 runs as 1e-30, which
   // changes no score by more than 1e-29 relative
   fp.scale_log2 = (scale > 0.0f ? scale : 1e-30f) * 1.4426950408889634f;
+  fp.dense_bytes = m->dense;
+  fp.dense_stride_b = m->dense_stride_b;
+  fp.dense_stride_h = m->dense_stride_h;
   fp.kv_splits = splits;
   if (splits > 1) {
     fp.o_part = (float*)((char*)workspace + fz.o_part_off);
@@ -320,14 +401,23 @@ attn_status attn_fwd_ex(const attn_problem* problem, const void* Q, const void* 
   if (p->dtype == ATTN_F32)
     return hip_status(timed(ATTN_KERNEL_FWD, s, [&] { return launch_fwd_f32(fp, p->head_dim, m->kind, s); }));
 
+  if (m->kind == ATTN_MASK_DENSE) {
+    // the dense mask becomes bits plus a block layout, which the planner and kernels then use
+    st = hip_status(timed(ATTN_KERNEL_MASK_PACK, s, [&] {
+      return pack_dense(p, m, fz.dense, (char*)workspace + fz.dense_off, false, &fp.dense, &fp.layout,
+                        &fp.layout_stride_b, &fp.layout_stride_h, s);
+    }));
+    if (st != ATTN_OK) return st;
+  }
   if (fz.plan_bytes > 0) {
     PlanParams pp;
     std::memset(&pp, 0, sizeof(pp));
-    pp.mode = PLAN_FWD_Q; pp.mask = m->kind; pp.heads = p->heads_q; pp.group = fp.group;
+    pp.mode = PLAN_FWD_Q; pp.mask = m->kind == ATTN_MASK_DENSE ? ATTN_MASK_BLOCK : m->kind;
+    pp.heads = p->heads_q; pp.group = fp.group;
     pp.seq_q = p->seq_q; pp.seq_k = p->seq_k; pp.n_tiles = fp.n_qtiles; pp.tile = bm;
     pp.n_items = fp.n_items; pp.nb_q = fp.nb_q; pp.nb_k = fp.nb_k;
-    pp.lengths = m->lengths; pp.layout = m->block_layout;
-    pp.layout_stride_b = m->layout_stride_b; pp.layout_stride_h = m->layout_stride_h;
+    pp.lengths = m->lengths; pp.layout = fp.layout;
+    pp.layout_stride_b = fp.layout_stride_b; pp.layout_stride_h = fp.layout_stride_h;
     pp.items = (uint32_t*)workspace;
     st = hip_status(timed(ATTN_KERNEL_PLAN, s, [&] { return launch_plan(pp, s); }));
     if (st != ATTN_OK) return st;
@@ -369,7 +459,7 @@ attn_status attn_bwd_ex(const attn_problem* problem, const void* Q, const void* 
   if ((flags & ~ATTN_BWD_ATOMIC_DQ) != 0) return ATTN_ERR_SHAPE;
   const bool atomic_dq = (flags & ATTN_BWD_ATOMIC_DQ) != 0;
   if (p->dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
-  if (m->kind == ATTN_MASK_BLOCK) {
+  if (m->kind == ATTN_MASK_BLOCK || m->kind == ATTN_MASK_DENSE) {
     // the dK/dV pass lists (query head, layout row) pairs of its column: 6 + 10 bits each
     const int64_t nbq = ceil_div(p->seq_q, 64), group = p->heads_q / p->heads_kv;
     if (nbq > 1024 || group > 63 || group * nbq > bwd_max_steps()) return ATTN_ERR_UNSUPPORTED;
@@ -403,6 +493,11 @@ attn_status attn_bwd_ex(const attn_problem* problem, const void* Q, const void* 
     for (const Range& r : outs)
       if (overlap(rlay, r)) return ATTN_ERR_ALIAS;
   }
+  if (m->kind == ATTN_MASK_DENSE) {
+    const Range rden = range_of(m->dense, (size_t)dense_bytes(p, m));
+    for (const Range& r : outs)
+      if (overlap(rden, r)) return ATTN_ERR_ALIAS;
+  }
 
   hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
@@ -425,11 +520,21 @@ attn_status attn_bwd_ex(const attn_problem* problem, const void* Q, const void* 
   bp.scale_log2 = (scale > 0.0f ? scale : 1e-30f) * 1.4426950408889634f;
   if (atomic_dq) bp.dq_acc = (float*)(ws + bs.dq_acc_off);
 
+  if (m->kind == ATTN_MASK_DENSE) {
+    // the dense mask becomes bits plus a block layout, which the planner and kernels then use
+    st = hip_status(timed(ATTN_KERNEL_MASK_PACK, s, [&] {
+      return pack_dense(p, m, bs.dense, ws + bs.dense_off, true, &bp.dense, &bp.layout, &bp.layout_stride_b,
+                        &bp.layout_stride_h, s);
+    }));
+    if (st != ATTN_OK) return st;
+  }
+
   PlanParams pp;
   std::memset(&pp, 0, sizeof(pp));
-  pp.mask = m->kind; pp.group = bp.group; pp.seq_q = p->seq_q; pp.seq_k = p->seq_k;
-  pp.nb_q = bp.nb_q; pp.nb_k = bp.nb_k; pp.lengths = m->lengths; pp.layout = m->block_layout;
-  pp.layout_stride_b = m->layout_stride_b; pp.layout_stride_h = m->layout_stride_h;
+  pp.mask = m->kind == ATTN_MASK_DENSE ? ATTN_MASK_BLOCK : m->kind;
+  pp.group = bp.group; pp.seq_q = p->seq_q; pp.seq_k = p->seq_k;
+  pp.nb_q = bp.nb_q; pp.nb_k = bp.nb_k; pp.lengths = m->lengths; pp.layout = bp.layout;
+  pp.layout_stride_b = bp.layout_stride_b; pp.layout_stride_h = bp.layout_stride_h;
   // dK/dV items (b, kv head, key tile) and dQ items (b, query head, query tile), one launch
   PlanParams pk = pp, pq = pp;
   pk.mode = PLAN_BWD_KV; pk.heads = p->heads_kv; pk.n_tiles = bs.n_kt; pk.tile = bs.bk;

@@ -98,7 +98,10 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) char d_st0[STATS];  // -Delta
   __shared__ __attribute__((aligned(16))) char l_st1[STATS];
   __shared__ __attribute__((aligned(16))) char d_st1[STATS];
-  __shared__ uint16_t list[MASK == MASK_BLOCK ? L::MAX_STEPS : 1];
+  // block and dense masks list the kept (query head, layout row) pairs of the key tile's column
+  // (a dense mask through its derived layout)
+  constexpr bool LISTED = MASK == MASK_BLOCK || MASK == MASK_DENSE;
+  __shared__ uint16_t list[LISTED ? L::MAX_STEPS : 1];
   __shared__ int list_count;
   // single-pass variant: each wave's dS of one 32-query block, [key][query] bf16, 64-byte rows
   __shared__ __attribute__((aligned(16))) char ds_t[ATOMIC_DQ ? NW * 2048 : 16];
@@ -150,7 +153,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdParams p) {
   if (key_tail) qt_f = qt_m;                 // every step masked
   qt_f = max(qt_f, qt_m);
   int n_free, n_steps;
-  if constexpr (MASK == MASK_BLOCK) {
+  if constexpr (LISTED) {
     const int col = k0 / 64;
     if (wave == 0) {
       int count = 0;
@@ -169,14 +172,14 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdParams p) {
     }
     __syncthreads();
     n_steps = list_count;
-    // ragged shapes run every step through the masked body
-    n_free = (key_tail || (p.seq_q % BQ) != 0) ? 0 : n_steps;
+    // ragged shapes run every step through the masked body, and so does a dense mask
+    n_free = (MASK == MASK_DENSE || key_tail || (p.seq_q % BQ) != 0) ? 0 : n_steps;
   } else {
     n_free = p.group * (qt_f - qt_m);
     n_steps = p.group * (qt_hi - qt_lo);
   }
   auto step_at = [&](int s, int& g, int& qt) __attribute__((always_inline)) {
-    if constexpr (MASK == MASK_BLOCK) {
+    if constexpr (LISTED) {
       const uint32_t e = list[s];
       g = (int)(e >> 10);
       qt = (int)(e & 1023u);
@@ -236,6 +239,12 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdParams p) {
     }
   }
 
+  // dense mask: bits of queries q0 + qb*32 .. +31 for this lane's key (0 past the key range)
+  auto dcol_word = [&](const uint32_t* dcol, int q0, int qb) __attribute__((always_inline)) -> uint32_t {
+    const int w = (q0 + qb * 32) >> 5;
+    return (my_k < p.seq_k && w < p.dense.col_words) ? dcol[w] : 0u;
+  };
+
   f32x16 dk[DB], dv[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
@@ -249,7 +258,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdParams p) {
   // P = exp2(scale log2(e) S - LSE log2(e)) and dS = P (dP - Delta), then dV += P^T dO and
   // dK += dS^T Q. The two blocks are software-pipelined so that the vector work of one block runs
   // under the MFMAs of the other: [S,dP 0] [S,dP 1 | P,dS 0] [dV,dK 0 | P,dS 1] [dV,dK 1].
-  auto body = [&](auto stage_tag, auto masked_tag, int q0) __attribute__((always_inline)) {
+  auto body = [&](auto stage_tag, auto masked_tag, int q0, const uint32_t* dcol) __attribute__((always_inline)) {
     constexpr int ST = decltype(stage_tag)::value;
     constexpr bool MASKED = decltype(masked_tag)::value;
     const char* ql = ST == 0 ? q_st0 : q_st1;
@@ -313,6 +322,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdParams p) {
           const int q = q0 + qb * 32 + hh * 16 + i;
           bool vis = q < q_len && my_k < kv_len;
           if constexpr (MASK == MASK_CAUSAL) vis = vis && my_k <= q;
+          if constexpr (MASK == MASK_DENSE) vis = vis && ((dcol_word(dcol, q0, qb) >> (hh * 16 + i)) & 1u);
           pv = vis ? pv : 0.0f;
         }
         pb[i >> 3][i & 7] = (bf16)pv;
@@ -396,7 +406,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdParams p) {
 
   // One step of the single-pass variant, one 32-query block at a time: the two-pass body's
   // products, then dQ_i += dS K_j for this wave's 32 keys, added to the fp32 accumulator.
-  auto body_atomic = [&](auto stage_tag, auto masked_tag, int q0, int hq) __attribute__((always_inline)) {
+  auto body_atomic = [&](auto stage_tag, auto masked_tag, int q0, int hq, const uint32_t* dcol)
+                         __attribute__((always_inline)) {
     constexpr int ST = decltype(stage_tag)::value;
     constexpr bool MASKED = decltype(masked_tag)::value;
     const char* ql = ST == 0 ? q_st0 : q_st1;
@@ -432,6 +443,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdParams p) {
           const int q = q0 + qbase + i;
           bool vis = q < q_len && my_k < kv_len;
           if constexpr (MASK == MASK_CAUSAL) vis = vis && my_k <= q;
+          if constexpr (MASK == MASK_DENSE) vis = vis && ((dcol_word(dcol, q0, qb) >> (hh * 16 + i)) & 1u);
           pv = vis ? pv : 0.0f;
         }
         pb[i >> 3][i & 7] = (bf16)pv;
@@ -496,9 +508,14 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdParams p) {
     int g, qt;
     step_at(s, g, qt);
     const int q0 = qt * BQ;
+    // dense mask: the column of bits of this lane's key for the step's query head
+    const uint32_t* dcol = MASK == MASK_DENSE
+        ? p.dense.cols + b * p.dense.cols_stride_b + (kvh * p.group + g) * p.dense.cols_stride_h +
+              (int64_t)min(my_k, p.seq_k - 1) * p.dense.col_words
+        : nullptr;
     auto run_body = [&]() __attribute__((always_inline)) {
-      if constexpr (ATOMIC_DQ) body_atomic(stage_tag, masked_tag, q0, kvh * p.group + g);
-      else body(stage_tag, masked_tag, q0);
+      if constexpr (ATOMIC_DQ) body_atomic(stage_tag, masked_tag, q0, kvh * p.group + g, dcol);
+      else body(stage_tag, masked_tag, q0, dcol);
     };
     if constexpr (!MASKED) {
       run_body();
@@ -559,7 +576,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
   __shared__ __attribute__((aligned(16))) char v_st0[L::TILE];
   __shared__ __attribute__((aligned(16))) char k_st1[L::TILE];
   __shared__ __attribute__((aligned(16))) char v_st1[L::TILE];
-  __shared__ uint32_t list[MASK == MASK_BLOCK ? L::MAX_LIST + 1 : 1];
+  constexpr bool LISTED = MASK == MASK_BLOCK || MASK == MASK_DENSE;
+  __shared__ uint32_t list[LISTED ? L::MAX_LIST + 1 : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -588,7 +606,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
     n_tiles = (q0 < q_len) ? (kv_len + BN - 1) / BN : 0;
   } else if constexpr (MASK == MASK_CAUSAL) {
     n_tiles = min((p.seq_k + BN - 1) / BN, (min(q0 + BM, p.seq_q) - 1) / BN + 1);
-  } else if constexpr (MASK == MASK_BLOCK) {
+  } else if constexpr (LISTED) {
     constexpr int ROWS = BM / 64 > 0 ? BM / 64 : 1;
     const uint8_t* lay = p.layout + b * p.layout_stride_b + h * p.layout_stride_h;
     const int r0 = q0 / 64;
@@ -626,6 +644,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
     dof[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rdo, off, 0, 0));
   }
   const size_t row_off = (size_t)(b * p.heads_q + h) * p.seq_q;
+  const uint32_t* dense_row = MASK == MASK_DENSE
+      ? p.dense.rows + b * p.dense.rows_stride_b + h * p.dense.rows_stride_h + (int64_t)my_q * p.dense.row_words
+      : nullptr;
   const float lse2 = my_q < p.seq_q ? p.lse2[row_off + my_q] : INFINITY;
   const float ndelta = my_q < p.seq_q ? p.delta[row_off + my_q] : 0.0f;   // -Delta
 
@@ -650,7 +671,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
   const float cs = p.scale_log2;
 
   auto tile_index = [&](int j) __attribute__((always_inline)) -> int {
-    if constexpr (MASK == MASK_BLOCK) return (int)(list[j] & 0xffffu);
+    if constexpr (LISTED) return (int)(list[j] & 0xffffu);
     return j;
   };
   auto issue_tile = [&](auto stage_tag, int kt) __attribute__((always_inline)) {
@@ -670,6 +691,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
     for (int kb = 0; kb < 2; ++kb) {
       f32x16 sc = f32x16{}, dp = f32x16{};
       bf16x8 ka[KS], va[KS];
+      // dense mask: the query's bits for keys k0 + kb*32 .. +31
+      uint32_t dw = 0;
+      if constexpr (MASK == MASK_DENSE) {
+        const int w = (k0 >> 5) + kb;
+        if (my_q < p.seq_q && w < p.dense.row_words) dw = dense_row[w];
+      }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         ka[ks] = *(const bf16x8*)(kl + roff[ks] + kb * 32 * RB);
@@ -708,6 +735,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
           const int key = k0 + kb * 32 + hh * 16 + i;
           bool vis = key < kv_len && my_q < q_len;
           if constexpr (MASK == MASK_CAUSAL) vis = vis && key <= my_q;
+          if constexpr (MASK == MASK_DENSE) vis = vis && ((dw >> (hh * 16 + i)) & 1u);
           pv = vis ? pv : 0.0f;
         }
         dsb[i >> 3][i & 7] = (bf16)(pv * (dp[i] + ndelta));
@@ -727,6 +755,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
     n_free = (q0 + BM <= q_len) ? kv_len / BN : 0;
   } else if constexpr (MASK == MASK_BLOCK) {
     n_free = (n_tiles > 0 && tile_index(n_tiles - 1) * BN + BN > p.seq_k) ? n_tiles - 1 : n_tiles;
+  } else if constexpr (MASK == MASK_DENSE) {
+    n_free = 0;   // every kept tile is tested pair by pair
   } else {
     n_free = p.seq_k / BN;
   }
@@ -741,13 +771,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
     const int k0 = tile_index(j) * BN;
     if constexpr (!MASKED) {
       bool active = true;
-      if constexpr (MASK == MASK_BLOCK && BM > 64) active = ((list[j] >> 16) >> ((wave * 32) / 64)) & 1u;
+      if constexpr (LISTED && BM > 64) active = ((list[j] >> 16) >> ((wave * 32) / 64)) & 1u;
       if (active) tile(stage_tag, masked_tag, k0);
     } else {
       bool active = k0 < kv_len;
       if constexpr (MASK == MASK_CAUSAL) active = active && k0 <= qw0 + 31;
       if constexpr (MASK == MASK_PADDING) active = active && qw0 < q_len;
-      if constexpr (MASK == MASK_BLOCK) active = ((list[j] >> 16) >> ((wave * 32) / 64)) & 1u;
+      if constexpr (LISTED) active = ((list[j] >> 16) >> ((wave * 32) / 64)) & 1u;
       if (active) tile(stage_tag, masked_tag, k0);
     }
   };
@@ -800,6 +830,7 @@ hipError_t dkdv_mask(const BwdParams& p, int mask, int n_items, hipStream_t s) {
       case MASK_NONE: return launch_dkdv_one<D, 4, MASK_NONE, true>(p, n_items, s);
       case MASK_CAUSAL: return launch_dkdv_one<D, 4, MASK_CAUSAL, true>(p, n_items, s);
       case MASK_PADDING: return launch_dkdv_one<D, 4, MASK_PADDING, true>(p, n_items, s);
+      case MASK_DENSE: return launch_dkdv_one<D, 2, MASK_DENSE, true>(p, n_items, s);
       default: return launch_dkdv_one<D, 2, MASK_BLOCK, true>(p, n_items, s);
     }
   }
@@ -807,6 +838,7 @@ hipError_t dkdv_mask(const BwdParams& p, int mask, int n_items, hipStream_t s) {
     case MASK_NONE: return launch_dkdv_one<D, 4, MASK_NONE>(p, n_items, s);
     case MASK_CAUSAL: return launch_dkdv_one<D, 4, MASK_CAUSAL>(p, n_items, s);
     case MASK_PADDING: return launch_dkdv_one<D, 4, MASK_PADDING>(p, n_items, s);
+    case MASK_DENSE: return launch_dkdv_one<D, 2, MASK_DENSE>(p, n_items, s);
     default: return launch_dkdv_one<D, 2, MASK_BLOCK>(p, n_items, s);
   }
 }
@@ -831,6 +863,7 @@ hipError_t dq_mask(const BwdParams& p, int mask, int n_items, hipStream_t s) {
     case MASK_NONE: return launch_dq_one<D, 4, MASK_NONE, 2>(p, n_items, s);
     case MASK_CAUSAL: return launch_dq_one<D, 4, MASK_CAUSAL, 2>(p, n_items, s);
     case MASK_PADDING: return launch_dq_one<D, 4, MASK_PADDING, 2>(p, n_items, s);
+    case MASK_DENSE: return launch_dq_one<D, 4, MASK_DENSE, 2>(p, n_items, s);
     default: return launch_dq_one<D, 4, MASK_BLOCK, 2>(p, n_items, s);
   }
 }
@@ -841,7 +874,10 @@ hipError_t dq_mask(const BwdParams& p, int mask, int n_items, hipStream_t s) {
 // union of their kept tiles and each wave pair computes only its own row's). dK/dV items are 128
 // keys, or one 64-key layout column for block masks (2 waves).
 int bwd_block_q(int head_dim, int mask) { (void)head_dim; (void)mask; return 128; }
-int bwd_block_k(int head_dim, int mask) { (void)head_dim; return mask == MASK_BLOCK ? 64 : 128; }
+int bwd_block_k(int head_dim, int mask) {
+  (void)head_dim;
+  return (mask == MASK_BLOCK || mask == MASK_DENSE) ? 64 : 128;
+}
 int bwd_max_steps() { return KvLds<128>::MAX_STEPS; }
 
 hipError_t launch_bwd_preprocess(const BwdParams& p, int head_dim, hipStream_t s) {

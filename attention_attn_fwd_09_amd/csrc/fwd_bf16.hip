@@ -52,7 +52,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
   __shared__ __attribute__((aligned(16))) char v_st0[L::TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char k_st1[L::TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char v_st1[L::TILE_BYTES];
-  __shared__ uint32_t list[MASK == MASK_BLOCK ? L::MAX_LIST + 1 : 1];
+  // block and dense masks walk a list of kept key tiles (a dense mask through its derived layout)
+  constexpr bool LISTED = MASK == MASK_BLOCK || MASK == MASK_DENSE;
+  __shared__ uint32_t list[LISTED ? L::MAX_LIST + 1 : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -73,6 +75,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
   const int q0 = it.t * BM;
   const int qw0 = q0 + wave * 32;
   const int my_q = qw0 + c;
+  // dense mask: this query's row of bits (only read when MASK_DENSE)
+  const uint32_t* dense_row = MASK == MASK_DENSE
+      ? p.dense.rows + b * p.dense.rows_stride_b + h * p.dense.rows_stride_h + (int64_t)my_q * p.dense.row_words
+      : nullptr;
 
   const size_t q_off = ((size_t)(b * p.heads_q + h) * p.seq_q) * D;
   const size_t kv_off = ((size_t)(b * p.heads_kv + kvh) * p.seq_k) * D;
@@ -91,7 +97,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
   } else if constexpr (MASK == MASK_CAUSAL) {
     const int last_q = min(q0 + BM, p.seq_q) - 1;
     n_tiles = min((p.seq_k + BN - 1) / BN, last_q / BN + 1);
-  } else if constexpr (MASK == MASK_BLOCK) {
+  } else if constexpr (LISTED) {
     // kept key tiles of the layout rows this workgroup covers, with one bit per 64-row layout row
     constexpr int ROWS = BM / 64 > 0 ? BM / 64 : 1;
     const uint8_t* lay = p.layout + b * p.layout_stride_b + h * p.layout_stride_h;
@@ -160,7 +166,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
   const float cs = p.scale_log2;
 
   auto tile_index = [&](int j) __attribute__((always_inline)) -> int {
-    if constexpr (MASK == MASK_BLOCK) return (int)(list[j] & 0xffffu);
+    if constexpr (LISTED) return (int)(list[j] & 0xffffu);
     return j;
   };
   auto issue_tile = [&](auto stage_tag, int kt) __attribute__((always_inline)) {
@@ -201,6 +207,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 
     // ---- mask (boundary tiles only): hidden scores become -inf ----
+    uint32_t dw0 = 0, dw1 = 0;   // dense mask: the query's bits for keys k0 .. k0+31, k0+32 .. k0+63
+    if constexpr (MASK == MASK_DENSE) {
+      if (my_q < p.seq_q) {
+        const int w = k0 >> 5;
+        dw0 = dense_row[w];
+        if (w + 1 < p.dense.row_words) dw1 = dense_row[w + 1];
+      }
+    }
     if constexpr (MASKED) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -213,6 +227,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
         if constexpr (MASK == MASK_PADDING) {
           v0 = v0 && my_q < q_len;
           v1 = v1 && my_q < q_len;
+        }
+        if constexpr (MASK == MASK_DENSE) {
+          v0 = v0 && ((dw0 >> (hh * 16 + i)) & 1u);
+          v1 = v1 && ((dw1 >> (hh * 16 + i)) & 1u);
         }
         s0[i] = v0 ? s0[i] : -INFINITY;
         s1[i] = v1 ? s1[i] : -INFINITY;
@@ -286,6 +304,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
     n_free = (q0 + BM <= q_len) ? kv_len / BN : 0;
   } else if constexpr (MASK == MASK_BLOCK) {
     n_free = (n_tiles > 0 && tile_index(n_tiles - 1) * BN + BN > p.seq_k) ? n_tiles - 1 : n_tiles;
+  } else if constexpr (MASK == MASK_DENSE) {
+    n_free = 0;   // every kept tile is tested pair by pair
   } else {
     n_free = p.seq_k / BN;
   }
@@ -308,14 +328,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
     const int k0 = tile_index(j) * BN;
     if constexpr (!MASKED) {
       bool active = true;
-      if constexpr (MASK == MASK_BLOCK && BM > 64) active = ((list[j] >> 16) >> ((wave * 32) / 64)) & 1u;
+      if constexpr (LISTED && BM > 64) active = ((list[j] >> 16) >> ((wave * 32) / 64)) & 1u;
       if (active) tile(stage_tag, masked_tag, k0);
     } else {
       // wave-uniform: does this wave see any key of the tile?
       bool active = k0 < kv_len;
       if constexpr (MASK == MASK_CAUSAL) active = active && k0 <= qw0 + 31;
       if constexpr (MASK == MASK_PADDING) active = active && qw0 < q_len;
-      if constexpr (MASK == MASK_BLOCK) active = ((list[j] >> 16) >> ((wave * 32) / 64)) & 1u;
+      if constexpr (LISTED) active = ((list[j] >> 16) >> ((wave * 32) / 64)) & 1u;
       if (active) tile(stage_tag, masked_tag, k0);
     }
   };
@@ -432,6 +452,7 @@ hipError_t launch_mask(const FwdParams& p, int mask, hipStream_t stream) {
     case MASK_NONE: return launch_one<D, NW, MASK_NONE, MW>(p, stream);
     case MASK_CAUSAL: return launch_one<D, NW, MASK_CAUSAL, MW>(p, stream);
     case MASK_PADDING: return launch_one<D, NW, MASK_PADDING, MW>(p, stream);
+    case MASK_DENSE: return launch_one<D, 4, MASK_DENSE, 2>(p, stream);
     default: return launch_one<D, 4, MASK_BLOCK, 2>(p, stream);
   }
 }
@@ -440,7 +461,7 @@ hipError_t launch_mask(const FwdParams& p, int mask, hipStream_t stream) {
 
 int fwd_bf16_block_m(int head_dim, int mask) {
   (void)head_dim;
-  return mask == MASK_BLOCK ? 128 : 32 * ATTN_FWD_NW;
+  return (mask == MASK_BLOCK || mask == MASK_DENSE) ? 128 : 32 * ATTN_FWD_NW;
 }
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int head_dim, int mask, hipStream_t stream) {

@@ -51,6 +51,11 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdParams p) {
   if constexpr (MASK == MASK_BLOCK) {
     lay_row = p.layout + b * p.layout_stride_b + h * p.layout_stride_h + (size_t)(q0 / 64) * p.nb_k;
   }
+  // dense mask: this query's row of bytes (queries past the end see nothing)
+  const uint8_t* dense_row = nullptr;
+  if constexpr (MASK == MASK_DENSE) {
+    dense_row = p.dense_bytes + b * p.dense_stride_b + h * p.dense_stride_h + (int64_t)min(my_q, p.seq_q - 1) * p.seq_k;
+  }
 
   // stage this tile's queries (rows past the end read as 0)
   for (int e = lane; e < BM32 * D; e += 64) {
@@ -93,6 +98,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdParams p) {
       bool vis = key < kv_len;
       if constexpr (MASK == MASK_CAUSAL) vis = vis && key <= my_q;
       if constexpr (MASK == MASK_PADDING) vis = vis && my_q < q_len;
+      if constexpr (MASK == MASK_DENSE) vis = vis && my_q < p.seq_q && dense_row[min(key, p.seq_k - 1)] != 0;
       s[j] = vis ? dot * cs : -INFINITY;
       mx = fmaxf(mx, s[j]);
     }
@@ -144,6 +150,7 @@ hipError_t launch_f32_mask(const FwdParams& p, int mask, hipStream_t stream) {
     case MASK_NONE: return launch_f32_one<D, MASK_NONE>(p, stream);
     case MASK_CAUSAL: return launch_f32_one<D, MASK_CAUSAL>(p, stream);
     case MASK_PADDING: return launch_f32_one<D, MASK_PADDING>(p, stream);
+    case MASK_DENSE: return launch_f32_one<D, MASK_DENSE>(p, stream);
     default: return launch_f32_one<D, MASK_BLOCK>(p, stream);
   }
 }

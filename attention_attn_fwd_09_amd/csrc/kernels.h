@@ -28,6 +28,19 @@ struct PlanParams {
   uint32_t* items;       // output: item ids, longest first
 };
 
+// Dense element mask -> row bits, column bits (optional) and a 64x64 block layout.
+struct DensePackParams {
+  const uint8_t* mask;          // caller's byte mask, [.., seq_q, seq_k]
+  int64_t stride_b, stride_h;   // elements between batch elements / query heads of the mask
+  int32_t batch_m, heads_m;     // distinct batch elements / heads of the mask (1 when shared)
+  int32_t seq_q, seq_k, nb_q, nb_k;
+  uint32_t* row_bits;           // [batch_m * heads_m][seq_q][row_words]
+  uint32_t* col_bits;           // [batch_m * heads_m][seq_k][col_words], or null
+  int32_t row_words, col_words;
+  uint8_t* layout;              // [batch_m * heads_m][nb_q][nb_k]
+};
+hipError_t launch_dense_pack(const DensePackParams& p, hipStream_t stream);
+
 hipError_t launch_plan(const PlanParams& p, hipStream_t stream);
 hipError_t launch_plan_pair(const PlanParams& a, const PlanParams& b, hipStream_t stream);
 

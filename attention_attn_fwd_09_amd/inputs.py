@@ -24,7 +24,7 @@ from typing import Optional
 
 import torch
 
-T_Q, T_K, T_V, T_DO, T_LEN, T_LAYOUT = range(6)
+T_Q, T_K, T_V, T_DO, T_LEN, T_LAYOUT, T_DENSE = range(7)
 
 
 @dataclass
@@ -82,7 +82,8 @@ def make_inputs(w: Workload, seed_base: int, with_do: bool = False) -> dict:
 
     Returns a dict with q, k, v (and do), lengths (int32 [batch] or None),
     layout (uint8 [nb_q, nb_k], or [batch, heads_q, nb_q, nb_k] when
-    ``w.layout_per_head``; None unless the mask is "block") and scale.
+    ``w.layout_per_head``; None unless the mask is "block"), dense (uint8
+    [seq_q, seq_k], or per (batch, head) likewise; only for the "dense" mask) and scale.
     """
     out = {
         "q": _normal((w.batch, w.heads_q, w.seq_q, w.head_dim), seed_base + T_Q, w.dtype),
@@ -106,6 +107,18 @@ def make_inputs(w: Workload, seed_base: int, with_do: bool = False) -> dict:
         diag = torch.arange(min(nbq, nbk))
         keep[..., diag, diag] = True
         out["layout"] = keep.to(torch.uint8).contiguous()
+    if w.mask == "dense":
+        # element mask: each pair kept with probability keep_prob, inside 64x64 blocks that are
+        # themselves kept with probability 0.7 (so whole blocks are hidden too)
+        shape = (w.batch, w.heads_q, w.seq_q, w.seq_k) if w.layout_per_head else (w.seq_q, w.seq_k)
+        g = _gen(seed_base + T_DENSE)
+        keep = torch.rand(*shape, generator=g) < w.keep_prob
+        nbq = -(-w.seq_q // w.block)
+        nbk = -(-w.seq_k // w.block)
+        blocks = torch.rand(*shape[:-2], nbq, nbk, generator=g) < 0.7
+        blocks = blocks.repeat_interleave(w.block, dim=-2).repeat_interleave(w.block, dim=-1)
+        keep &= blocks[..., :w.seq_q, :w.seq_k]
+        out["dense"] = keep.to(torch.uint8).contiguous()
     return out
 
 

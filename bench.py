@@ -27,7 +27,8 @@ import time
 METRIC = "attention fwd/bwd TFLOP/s (bf16) + % of MFMA peak on 1 MI355X, seq 2048-8192"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-KERNEL_NAMES = {0: "plan", 1: "fwd", 2: "bwd_pre", 3: "bwd_dkdv", 4: "bwd_dq", 5: "fwd_merge", 6: "bwd_dq_convert"}
+KERNEL_NAMES = {0: "plan", 1: "fwd", 2: "bwd_pre", 3: "bwd_dkdv", 4: "bwd_dq", 5: "fwd_merge", 6: "bwd_dq_convert",
+                7: "mask_pack"}
 
 
 def log(msg: str):
@@ -307,7 +308,7 @@ def cpu_baseline(w, inp, pairs_total):
             "seconds": round(secs, 2)}
 
 
-def time_calls(torch, fn, n=20, warm=5):
+def time_calls(torch, fn, n=20, warm=10):
     """Median, min and mean milliseconds of n calls of fn after warm untimed calls (one event pair
     per call on the current stream)."""
     for _ in range(warm):
@@ -325,7 +326,7 @@ def time_calls(torch, fn, n=20, warm=5):
 
 def forward_all(lib, torch, dev, workloads, workload_inputs):
     """Extra diagnostics on stderr: forward-only TFLOP/s of every measured workload (median of 20
-    calls after 5 warm-up calls; min and mean alongside), then split-KV against no split on shapes
+    calls after 10 warm-up calls; min and mean alongside), then split-KV against no split on shapes
     with few work items."""
     for cfg, w in workloads.items():
         inp = workload_inputs(cfg)
@@ -343,6 +344,33 @@ def forward_all(lib, torch, dev, workloads, workload_inputs):
                         "pct_peak": round(100 * fl / med / 1e9 / PEAK_BF16_TFLOPS, 2)}))
     split_kv_diag(lib, torch, dev)
     bwd_modes_diag(lib, torch, dev, workloads, workload_inputs)
+    dense_mask_diag(lib, torch, dev)
+
+
+def dense_mask_diag(lib, torch, dev):
+    """Forward and backward under a dense element mask at the block-sparse workload's shape (pairs
+    kept with p = 0.5 inside 64x64 blocks kept with p = 0.7); the pack of the mask to bits and a
+    block layout is inside every call."""
+    from attention_attn_fwd_09_amd.inputs import Workload, make_inputs
+
+    w = Workload("fwdbwd_bf16_b2_h16_s4096_d128_dense_p05", "bf16", 2, 16, 16, 4096, 4096, 128, "dense",
+                 backward=True, keep_prob=0.5)
+    inp = make_inputs(w, 8000)
+    q, k, v, do = (inp[x].to(dev).contiguous() for x in ("q", "k", "v", "do"))
+    m = lib.Mask(kind="dense", dense=inp["dense"].to(dev).contiguous())
+    pairs = int(inp["dense"].to(torch.int64).sum()) * w.batch * w.heads_q
+    wsf = torch.empty(max(1, lib.attn_fwd_workspace_bytes(q, k, m)), dtype=torch.uint8, device=dev)
+    wsb = torch.empty(max(1, lib.attn_bwd_workspace_bytes(q, k, m)), dtype=torch.uint8, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    fmed, _, _ = time_calls(torch, lambda: lib.attn_fwd(q, k, v, mask=m, scale=inp["scale"], out=o, lse=lse,
+                                                         workspace=wsf))
+    bmed, _, _ = time_calls(torch, lambda: lib.attn_bwd(q, k, v, o, do, lse, mask=m, scale=inp["scale"], dq=dq, dk=dk,
+                                                         dv=dv, workspace=wsb))
+    log(json.dumps({"workload": w.name, "visible_pairs": pairs, "fwd_ms": round(fmed, 5),
+                    "fwd_tflops": round(4 * w.head_dim * pairs / fmed / 1e9, 2), "bwd_ms": round(bmed, 5),
+                    "bwd_tflops": round(10 * w.head_dim * pairs / bmed / 1e9, 2)}))
 
 
 def bwd_modes_diag(lib, torch, dev, workloads, workload_inputs):

@@ -73,7 +73,8 @@ typedef enum {
   ATTN_MASK_NONE = 0,    /* every key visible */
   ATTN_MASK_CAUSAL = 1,  /* key j hidden from query i when j > i; needs seq_q == seq_k */
   ATTN_MASK_PADDING = 2, /* per batch element b: (i, j) visible iff i < len[b] and j < len[b] */
-  ATTN_MASK_BLOCK = 3    /* block_q x block_k tiles kept where the layout byte is non-zero */
+  ATTN_MASK_BLOCK = 3,   /* block_q x block_k tiles kept where the layout byte is non-zero */
+  ATTN_MASK_DENSE = 4    /* (i, j) visible iff the dense mask byte is non-zero */
 } attn_mask_kind;
 
 /* Sizes of one attention problem. dtype is an attn_dtype value. */
@@ -93,6 +94,14 @@ typedef struct {
  *               layout across batch elements and/or heads. A tile on a ragged
  *               edge covers only the rows/columns that exist.
  *  block_q, block_k  BLOCK: tile sizes; this build supports 64 x 64.
+ *  dense        DENSE: device uint8, one [seq_q][seq_k] row-major matrix per
+ *               (b, h) at element offset b*dense_stride_b + h*dense_stride_h
+ *               (h = query head); 0 = the score becomes -infinity, non-zero =
+ *               visible. This is the generic mask[i][j] of the fused
+ *               multi-head attention operator write-up (zwxr.cn), section 3.3.
+ *               Strides of 0 share one mask across batch elements and/or heads.
+ *               Each call packs it once to bits and a 64x64 block layout in
+ *               the workspace, so blocks it hides entirely are never visited.
  * Pointers a kind does not use are ignored and may be NULL.
  */
 typedef struct {
@@ -101,6 +110,8 @@ typedef struct {
   const uint8_t *block_layout;
   int64_t layout_stride_b, layout_stride_h;
   int32_t block_q, block_k;
+  const uint8_t *dense;
+  int64_t dense_stride_b, dense_stride_h;
 } attn_mask;
 
 /* Bytes of workspace attn_fwd needs for this problem and mask (0 if none). Equal to
@@ -198,7 +209,8 @@ typedef enum {
   ATTN_KERNEL_BWD_DQ = 4,   /* backward dQ pass */
   ATTN_KERNEL_FWD_MERGE = 5, /* split-KV merge of the forward */
   ATTN_KERNEL_BWD_DQ_CONVERT = 6, /* single-pass backward: dQ accumulator to bf16 */
-  ATTN_KERNEL_CLASSES = 7
+  ATTN_KERNEL_MASK_PACK = 7, /* dense mask to bits and a block layout */
+  ATTN_KERNEL_CLASSES = 8
 } attn_kernel_class;
 /*
  * While set for a class, each launch of that class records start_events[i] before it and

@@ -31,7 +31,10 @@ def to_np64(t: torch.Tensor) -> np.ndarray:
 def oracle_mask(w: Workload, inp: dict) -> oracle.MaskSpec:
     lengths = inp["lengths"].numpy() if inp["lengths"] is not None else None
     layout = inp["layout"].numpy() if inp["layout"] is not None else None
-    return oracle.MaskSpec(kind=w.mask, lengths=lengths, layout=layout, block_q=w.block, block_k=w.block)
+    spec = oracle.MaskSpec(kind=w.mask, lengths=lengths, layout=layout, block_q=w.block, block_k=w.block)
+    if inp.get("dense") is not None:
+        spec.dense = inp["dense"].numpy()
+    return spec
 
 
 def device_inputs(inp: dict, dev="cuda") -> dict:
@@ -42,7 +45,8 @@ def device_inputs(inp: dict, dev="cuda") -> dict:
 
 
 def lib_mask(w: Workload, dinp: dict) -> libattn.Mask:
-    return libattn.Mask(kind=w.mask, lengths=dinp["lengths"], layout=dinp["layout"], block=w.block)
+    return libattn.Mask(kind=w.mask, lengths=dinp["lengths"], layout=dinp["layout"], block=w.block,
+                        dense=dinp.get("dense"))
 
 
 def run_fwd(w: Workload, seed: int):

@@ -191,7 +191,9 @@ def test_bwd_rejections():
 def test_timing_hook_argument_checks():
     lib = _lib()
     assert lib.attn_set_timing_events(-1, None, None, 0, None) == B.ATTN_ERR_SHAPE
-    assert lib.attn_set_timing_events(7, None, None, 0, None) == B.ATTN_ERR_SHAPE
+    n_classes = int(re.search(r"ATTN_KERNEL_CLASSES\s*=\s*(\d+)", open(HEADER).read()).group(1))
+    assert lib.attn_set_timing_events(n_classes, None, None, 0, None) == B.ATTN_ERR_SHAPE
+    assert lib.attn_set_timing_events(n_classes - 1, None, None, 0, None) == B.ATTN_OK
     arr = (ctypes.c_void_p * 1)()
     assert lib.attn_set_timing_events(1, arr, arr, 1, None) == B.ATTN_ERR_NULL
     assert lib.attn_set_timing_events(1, None, None, 0, None) == B.ATTN_OK
@@ -261,3 +263,25 @@ def test_single_pass_backward_arguments():
     assert call(-1, 1 << 40) == B.ATTN_ERR_SHAPE
     assert call(B.ATTN_BWD_ATOMIC_DQ, one - 1) == B.ATTN_ERR_WORKSPACE
     assert call(B.ATTN_BWD_ATOMIC_DQ, two) == B.ATTN_ERR_WORKSPACE
+
+
+def test_dense_mask_arguments():
+    lib = _lib()
+    ptr = _fwd_ok_ptrs()
+    kw = dict(q=ptr["q"], k=ptr["k"], v=ptr["v"], o=ptr["o"], lse=ptr["lse"])
+    m = _mask(kind=4)
+    assert _fwd(lib, _problem(), m, **kw) == B.ATTN_ERR_MASK                 # no dense pointer
+    m.dense = _spaced(7)[6]
+    m.dense_stride_b = -1
+    assert _fwd(lib, _problem(), m, **kw) == B.ATTN_ERR_MASK                 # negative stride
+    m.dense_stride_b = 0
+    # rectangular problems are fine for a dense mask; the bf16 forward packs it in the workspace
+    p = _problem(sq=100, sk=300)
+    need = lib.attn_fwd_workspace_bytes(ctypes.byref(p), ctypes.byref(m))
+    assert need >= 100 * ((300 + 31) // 32) * 4 + 2 * 5
+    assert _fwd(lib, p, m, **kw) == B.ATTN_ERR_WORKSPACE
+    # the fp32 forward reads the bytes directly and needs no workspace
+    assert lib.attn_fwd_workspace_bytes(ctypes.byref(_problem(dtype=B.ATTN_F32)), ctypes.byref(m)) == 0
+    # the mask is an input: an output overlapping it is rejected
+    m.dense = ptr["o"] + 64
+    assert _fwd(lib, p, m, ws=ptr["ws"], ws_bytes=need, **kw) == B.ATTN_ERR_ALIAS
