@@ -55,6 +55,7 @@ __all__ = [
     "attention_rows",
     "attention_bwd",
     "attention_bwd_head",
+    "attention_dq_rows",
 ]
 
 
@@ -188,6 +189,32 @@ def attention_rows(q, k, v, mask: MaskSpec, scale: float, b: int, h: int, rows):
     with np.errstate(divide="ignore"):
         lse = np.where(nonempty, m + np.log(safe), -np.inf)
     return o, lse
+
+
+def attention_dq_rows(q, k, v, do, mask: MaskSpec, scale: float, b: int, h: int, rows):
+    """dQ of selected query rows of one (b, h) pair: the chain rule of attention_bwd restricted to
+    those rows (row i of dQ needs only row i of P, dP and dS), for sampling very long sequences."""
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    do = np.asarray(do)
+    rows = np.asarray(rows)
+    hq, hkv = q.shape[1], k.shape[1]
+    g = _kv_head(h, hq, hkv)
+    sq, sk = q.shape[2], k.shape[2]
+    keep = mask_matrix(mask, b, h, sq, sk)[rows]
+    qr = np.asarray(q[b, h, rows], dtype=np.float64)
+    dor = np.asarray(do[b, h, rows], dtype=np.float64)
+    kg = np.asarray(k[b, g], dtype=np.float64)
+    vg = np.asarray(v[b, g], dtype=np.float64)
+    s = np.where(keep, scale * (qr @ kg.T), -np.inf)
+    nonempty = keep.any(axis=1)
+    m = np.where(nonempty, s.max(axis=1, initial=-np.inf), 0.0)
+    e = np.where(keep, np.exp(s - m[:, None]), 0.0)
+    p = e / np.where(nonempty, e.sum(axis=1), 1.0)[:, None]
+    dp = dor @ vg.T
+    ds = p * (dp - (p * dp).sum(axis=1)[:, None])
+    return scale * (ds @ kg)
 
 
 def attention_bwd(q, k, v, do, mask: MaskSpec, scale: float):

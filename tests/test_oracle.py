@@ -109,3 +109,24 @@ def test_bwd_head_matches_full_oracle():
                 dv_sum[b, h // 2] += dv_h
         np.testing.assert_allclose(dk_sum, dk, rtol=0, atol=1e-13)
         np.testing.assert_allclose(dv_sum, dv, rtol=0, atol=1e-13)
+
+
+def test_dq_rows_match_full_oracle():
+    """attention_dq_rows is attention_bwd's dQ restricted to a subset of rows."""
+    import numpy as np
+
+    r = np.random.default_rng(5)
+    q, k, v = r.standard_normal((2, 4, 70, 8)), r.standard_normal((2, 2, 70, 8)), r.standard_normal((2, 2, 70, 8))
+    do = r.standard_normal(q.shape)
+    lay = (r.random((2, 2)) < 0.5).astype(np.uint8)
+    dense = (r.random((70, 70)) < 0.4).astype(np.uint8)
+    specs = [oracle.MaskSpec("none"), oracle.MaskSpec("causal"),
+             oracle.MaskSpec("padding", lengths=np.array([30, 70], np.int32)),
+             oracle.MaskSpec("block", layout=lay), oracle.MaskSpec("dense", dense=dense)]
+    rows = np.array([0, 5, 31, 63, 64, 69])
+    for spec in specs:
+        dq, _, _ = oracle.attention_bwd(q, k, v, do, spec, 0.3)
+        for b in range(2):
+            for h in range(4):
+                got = oracle.attention_dq_rows(q, k, v, do, spec, 0.3, b, h, rows)
+                np.testing.assert_allclose(got, dq[b, h, rows], rtol=0, atol=1e-13)
