@@ -83,16 +83,18 @@ class MaskSpec:
     dense: Optional[np.ndarray] = None
 
 
-def mask_matrix(spec: MaskSpec, b: int, h: int, sq: int, sk: int) -> np.ndarray:
-    """Dense boolean [sq, sk] matrix for batch element b and query head h.
+def mask_matrix(spec: MaskSpec, b: int, h: int, sq: int, sk: int, rows=None) -> np.ndarray:
+    """Dense boolean [sq, sk] matrix for batch element b and query head h (only the query rows
+    ``rows`` of it, in that order, when given).
 
     True means query i attends to key j; False means the score is replaced by
     minus infinity (page 2, section 3.3: mask value 0 -> -inf).
     """
-    i = np.arange(sq)[:, None]
+    qi = np.arange(sq) if rows is None else np.asarray(rows)
+    i = qi[:, None]
     j = np.arange(sk)[None, :]
     if spec.kind == "none":
-        return np.ones((sq, sk), dtype=bool)
+        return np.ones((len(qi), sk), dtype=bool)
     if spec.kind == "causal":
         return j <= i
     if spec.kind == "padding":
@@ -103,14 +105,14 @@ def mask_matrix(spec: MaskSpec, b: int, h: int, sq: int, sk: int) -> np.ndarray:
         if lay.ndim == 4:
             lay = lay[b, h]
         keep = lay != 0
-        rows = np.minimum(np.arange(sq) // spec.block_q, keep.shape[0] - 1)
-        cols = np.minimum(np.arange(sk) // spec.block_k, keep.shape[1] - 1)
-        return keep[rows[:, None], cols[None, :]]
+        brows = np.minimum(qi // spec.block_q, keep.shape[0] - 1)
+        bcols = np.minimum(np.arange(sk) // spec.block_k, keep.shape[1] - 1)
+        return keep[brows[:, None], bcols[None, :]]
     if spec.kind == "dense":
         arr = np.asarray(spec.dense)
         if arr.ndim == 4:
             arr = arr[b, h]
-        return arr[:sq, :sk] != 0
+        return arr[:sq, :sk][qi] != 0
     raise ValueError(f"unknown mask kind {spec.kind!r}")
 
 
@@ -175,7 +177,7 @@ def attention_rows(q, k, v, mask: MaskSpec, scale: float, b: int, h: int, rows):
     hq, hkv = q.shape[1], k.shape[1]
     g = _kv_head(h, hq, hkv)
     sq, sk = q.shape[2], k.shape[2]
-    keep = mask_matrix(mask, b, h, sq, sk)[rows]
+    keep = mask_matrix(mask, b, h, sq, sk, rows)
     qr = np.asarray(q[b, h, rows], dtype=np.float64)
     kg = np.asarray(k[b, g], dtype=np.float64)
     vg = np.asarray(v[b, g], dtype=np.float64)
@@ -202,7 +204,7 @@ def attention_dq_rows(q, k, v, do, mask: MaskSpec, scale: float, b: int, h: int,
     hq, hkv = q.shape[1], k.shape[1]
     g = _kv_head(h, hq, hkv)
     sq, sk = q.shape[2], k.shape[2]
-    keep = mask_matrix(mask, b, h, sq, sk)[rows]
+    keep = mask_matrix(mask, b, h, sq, sk, rows)
     qr = np.asarray(q[b, h, rows], dtype=np.float64)
     dor = np.asarray(do[b, h, rows], dtype=np.float64)
     kg = np.asarray(k[b, g], dtype=np.float64)

@@ -33,10 +33,12 @@ MUTANTS = {
     "dq_scale_dropped": ("dq[b, h] = scale * (ds @ k[b, g])", "dq[b, h] = (ds @ k[b, g])"),
     "dk_transposed": ("dk[b, g] += scale * (ds.T @ q[b, h])", "dk[b, g] += scale * (ds @ q[b, h])"),
     "dk_overwrite_group": ("dk[b, g] += scale", "dk[b, g] = scale"),
-    "block_rows_cols_swapped": ("return keep[rows[:, None], cols[None, :]]", "return keep.T[rows[:, None], cols[None, :]]"),
-    "dense_transposed": ("return arr[:sq, :sk] != 0", "return arr.T[:sq, :sk] != 0"),
-    "dense_inverted": ("return arr[:sq, :sk] != 0", "return arr[:sq, :sk] == 0"),
-    "dense_head_ignored": ("        arr = arr[b, h]\n        return arr[:sq, :sk] != 0", "        arr = arr[0, 0]\n        return arr[:sq, :sk] != 0"),
+    "block_rows_cols_swapped": ("return keep[brows[:, None], bcols[None, :]]",
+                                "return keep.T[brows[:, None], bcols[None, :]]"),
+    "dense_transposed": ("return arr[:sq, :sk][qi] != 0", "return arr.T[:sq, :sk][qi] != 0"),
+    "dense_inverted": ("return arr[:sq, :sk][qi] != 0", "return arr[:sq, :sk][qi] == 0"),
+    "dense_head_ignored": ("        arr = arr[b, h]\n        return arr[:sq, :sk][qi] != 0",
+                           "        arr = arr[0, 0]\n        return arr[:sq, :sk][qi] != 0"),
 }
 
 
