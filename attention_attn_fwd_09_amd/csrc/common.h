@@ -127,6 +127,7 @@ __device__ __forceinline__ int sigma32(int r) { return ((r >> 2) & 1) * 16 + (r 
 // NaN-propagating maximum (v_maximum3_f32 on gfx950). fmaxf would first quiet every operand the
 // compiler cannot prove canonical (one extra VALU op per MFMA result).
 __device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float vmax3(float a, float b, float c) { return vmax(vmax(a, b), c); }
 
 // acc + sum of the 8 bf16 values of x, in fp32, four v_dot2 ops against (1, 1)
 __device__ __forceinline__ float sum_bf16x8(bf16x8 x, float acc) {

@@ -238,10 +238,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
     }
 
     // ---- online softmax on this lane's 32 scores (keys k0 + kb*32 + hh*16 + i) ----
-    float mx = -INFINITY;
+    // two chains of three-input maxima (one per key block), then their maximum
+    float ma = vmax(s0[0], s0[1]), mb = vmax(s1[0], s1[1]);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mx = vmax(mx, vmax(s0[i], s1[i]));
-    mx = partner_max(mx) * cs;   // cs > 0, so max(s) * cs = max(s * cs); -inf stays -inf
+    for (int i = 2; i < 16; i += 2) {
+      ma = vmax3(ma, s0[i], s0[i + 1]);
+      mb = vmax3(mb, s1[i], s1[i + 1]);
+    }
+    float mx = partner_max(vmax(ma, mb)) * cs;   // cs > 0, so max(s) * cs = max(s * cs); -inf stays -inf
     if (__builtin_expect(__ballot(mx > m_run + RESCALE_SLACK) != 0, 0)) {
       const float m_new = vmax(m_run, mx);
       const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_run - m_new);
