@@ -31,6 +31,7 @@ ATTN_ERR_HIP = 9
 
 ATTN_F32 = 0
 ATTN_BF16 = 1
+ATTN_FP8_E4M3 = 2  # forward inputs only; O is bf16
 
 ATTN_BWD_ATOMIC_DQ = 1  # attn_bwd_ex flag: single-pass backward with atomic fp32 dQ accumulation
 
@@ -149,6 +150,8 @@ def _dtype_code(t: torch.Tensor) -> int:
         return ATTN_F32
     if t.dtype == torch.bfloat16:
         return ATTN_BF16
+    if t.dtype == torch.float8_e4m3fn:
+        return ATTN_FP8_E4M3
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
@@ -217,7 +220,8 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Optional[M
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[-1])
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty(q.shape, dtype=torch.bfloat16 if q.dtype == torch.float8_e4m3fn else q.dtype,
+                          device=q.device)
     if lse is None:
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     need = int(lib.attn_fwd_ex_workspace_bytes(ctypes.byref(prob), ctypes.byref(cm), int(kv_splits)))

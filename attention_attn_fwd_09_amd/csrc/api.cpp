@@ -23,7 +23,9 @@ constexpr int MAX_BLOCK_COLS = 1024;  // key tiles per layout row the forward ke
 
 size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
-size_t elem_size(int32_t dtype) { return dtype == ATTN_F32 ? 4 : 2; }
+// bytes of one input element, and of one output (O) element: fp8 inputs give a bf16 output
+size_t elem_size(int32_t dtype) { return dtype == ATTN_F32 ? 4 : dtype == ATTN_FP8_E4M3 ? 1 : 2; }
+size_t out_elem_size(int32_t dtype) { return dtype == ATTN_F32 ? 4 : 2; }
 
 struct Range {
   uintptr_t lo, hi;  // [lo, hi)
@@ -41,7 +43,7 @@ attn_status check_problem(const attn_problem* p, const attn_mask* m, float scale
   if (p->batch < 1 || p->heads_q < 1 || p->heads_kv < 1 || p->seq_q < 1 || p->seq_k < 1 || p->head_dim < 1)
     return ATTN_ERR_SHAPE;
   if (p->heads_q % p->heads_kv != 0) return ATTN_ERR_SHAPE;
-  if (p->dtype != ATTN_F32 && p->dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+  if (p->dtype != ATTN_F32 && p->dtype != ATTN_BF16 && p->dtype != ATTN_FP8_E4M3) return ATTN_ERR_DTYPE;
   if (!(std::isfinite(scale) && scale >= 0.0f)) return ATTN_ERR_SHAPE;
   switch (m->kind) {
     case ATTN_MASK_NONE: break;
@@ -92,7 +94,7 @@ struct DenseSizes {
 
 DenseSizes dense_sizes(const attn_problem* p, const attn_mask* m, bool with_cols) {
   DenseSizes z{};
-  if (m->kind != ATTN_MASK_DENSE || p->dtype != ATTN_BF16) return z;
+  if (m->kind != ATTN_MASK_DENSE || p->dtype == ATTN_F32) return z;
   z.batch_m = m->dense_stride_b != 0 ? p->batch : 1;
   z.heads_m = m->dense_stride_h != 0 ? p->heads_q : 1;
   z.row_words = ceil_div(p->seq_k, 32);
@@ -138,11 +140,13 @@ hipError_t pack_dense(const attn_problem* p, const attn_mask* m, const DenseSize
 }
 
 int fwd_tile_m(const attn_problem* p, const attn_mask* m) {
-  return p->dtype == ATTN_F32 ? fwd_f32_block_m() : fwd_bf16_block_m(p->head_dim, m->kind);
+  if (p->dtype == ATTN_F32) return fwd_f32_block_m();
+  if (p->dtype == ATTN_FP8_E4M3) return fwd_fp8_block_m();
+  return fwd_bf16_block_m(p->head_dim, m->kind);
 }
 
 bool fwd_needs_plan(const attn_problem* p, const attn_mask* m) {
-  return p->dtype == ATTN_BF16 &&
+  return p->dtype != ATTN_F32 &&
          (m->kind == ATTN_MASK_PADDING || m->kind == ATTN_MASK_BLOCK || m->kind == ATTN_MASK_DENSE);
 }
 
@@ -160,7 +164,7 @@ constexpr int kMaxSplits = 32;
 constexpr int64_t kCUs = 256;
 constexpr int64_t kWorkgroupSlots = 512;
 int32_t fwd_splits(const attn_problem* p, const attn_mask* m, int32_t requested) {
-  if (p->dtype != ATTN_BF16 || requested == 1) return 1;
+  if (p->dtype == ATTN_F32 || requested == 1) return 1;
   const int32_t kv_tiles = ceil_div(p->seq_k, 64);
   if (requested > 1) return std::max(1, std::min(requested, kv_tiles));
   const int64_t items = fwd_items(p, m);
@@ -193,7 +197,7 @@ FwdSizes fwd_sizes(const attn_problem* p, const attn_mask* m, int32_t splits) {
 
 attn_status check_splits(const attn_problem* p, const attn_mask* m, int32_t requested) {
   if (requested < 0 || requested > kMaxSplits) return ATTN_ERR_SHAPE;
-  if (requested > 1 && p->dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (requested > 1 && p->dtype == ATTN_F32) return ATTN_ERR_UNSUPPORTED;
   if (fwd_items(p, m) * fwd_splits(p, m, requested) >= (int64_t(1) << 31)) return ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
 }
@@ -281,7 +285,7 @@ const char* attn_status_string(attn_status s) {
   return "unknown status";
 }
 
-int32_t attn_version(void) { return 102; }
+int32_t attn_version(void) { return 103; }
 
 attn_status attn_set_timing_events(int32_t kernel_class, void* const* start_events, void* const* stop_events,
                                    int32_t capacity, int32_t* count) {
@@ -345,7 +349,8 @@ attn_status attn_fwd_ex(const attn_problem* problem, const void* Q, const void* 
   const size_t qbytes = (size_t)p->batch * p->heads_q * p->seq_q * p->head_dim * es;
   const size_t kvbytes = (size_t)p->batch * p->heads_kv * p->seq_k * p->head_dim * es;
   const Range rq = range_of(Q, qbytes), rk = range_of(K, kvbytes), rv = range_of(V, kvbytes);
-  const Range ro = range_of(O, qbytes), rl = range_of(LSE, (size_t)p->batch * p->heads_q * p->seq_q * 4);
+  const size_t obytes = (size_t)p->batch * p->heads_q * p->seq_q * p->head_dim * out_elem_size(p->dtype);
+  const Range ro = range_of(O, obytes), rl = range_of(LSE, (size_t)p->batch * p->heads_q * p->seq_q * 4);
   const Range rw = range_of(workspace, need);
   for (Range out : {ro, rl}) {
     if (overlap(out, rq) || overlap(out, rk) || overlap(out, rv)) return ATTN_ERR_ALIAS;
@@ -423,7 +428,10 @@ attn_status attn_fwd_ex(const attn_problem* problem, const void* Q, const void* 
     if (st != ATTN_OK) return st;
     fp.items = (const uint32_t*)workspace;
   }
-  st = hip_status(timed(ATTN_KERNEL_FWD, s, [&] { return launch_fwd_bf16(fp, p->head_dim, m->kind, s); }));
+  if (p->dtype == ATTN_FP8_E4M3)
+    st = hip_status(timed(ATTN_KERNEL_FWD, s, [&] { return launch_fwd_fp8(fp, p->head_dim, m->kind, s); }));
+  else
+    st = hip_status(timed(ATTN_KERNEL_FWD, s, [&] { return launch_fwd_bf16(fp, p->head_dim, m->kind, s); }));
   if (st != ATTN_OK || splits == 1) return st;
   return hip_status(timed(ATTN_KERNEL_FWD_MERGE, s, [&] { return launch_fwd_merge(fp, p->head_dim, s); }));
 }

@@ -22,6 +22,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "fwd_shared.h"
 #include "kernels.h"
 
 namespace attn {
@@ -86,46 +87,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
   const __amdgpu_buffer_rsrc_t rk = make_rsrc((const bf16*)p.k + kv_off, (uint32_t)p.seq_k * RB);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc((const bf16*)p.v + kv_off, (uint32_t)p.seq_k * RB);
 
-  // ---- key range of this item ----
-  int kv_len = p.seq_k;   // keys at or beyond kv_len are masked
-  int q_len = p.seq_q;    // queries at or beyond q_len see nothing
-  int n_tiles;
-  if constexpr (MASK == MASK_PADDING) {
-    kv_len = clamp_len(p.lengths[b], p.seq_k);
-    q_len = clamp_len(p.lengths[b], p.seq_q);
-    n_tiles = (q0 < q_len) ? (kv_len + BN - 1) / BN : 0;
-  } else if constexpr (MASK == MASK_CAUSAL) {
-    const int last_q = min(q0 + BM, p.seq_q) - 1;
-    n_tiles = min((p.seq_k + BN - 1) / BN, last_q / BN + 1);
-  } else if constexpr (LISTED) {
-    // kept key tiles of the layout rows this workgroup covers, with one bit per 64-row layout row
-    constexpr int ROWS = BM / 64 > 0 ? BM / 64 : 1;
-    const uint8_t* lay = p.layout + b * p.layout_stride_b + h * p.layout_stride_h;
-    const int r0 = q0 / 64;
-    if (wave == 0) {
-      int count = 0;
-      for (int j0 = 0; j0 < p.nb_k; j0 += 64) {
-        const int j = j0 + lane;
-        uint32_t bits = 0;
-        if (j < p.nb_k) {
-#pragma unroll
-          for (int r = 0; r < ROWS; ++r) {
-            const int row = r0 + r;
-            if (row < p.nb_q && lay[(size_t)row * p.nb_k + j] != 0) bits |= 1u << r;
-          }
-        }
-        const uint64_t ball = __ballot(bits != 0);
-        const int before = __builtin_amdgcn_mbcnt_hi((uint32_t)(ball >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ball, 0));
-        if (bits != 0) list[count + before] = (uint32_t)j | (bits << 16);
-        count += __popcll(ball);
-      }
-      if (lane == 0) list[L::MAX_LIST] = (uint32_t)count;
-    }
-    __syncthreads();
-    n_tiles = (int)list[L::MAX_LIST];
-  } else {
-    n_tiles = (p.seq_k + BN - 1) / BN;
-  }
+  // ---- key tiles this item walks ----
+  int kv_len, q_len;
+  const int n_tiles = fwd_key_tiles<MASK, BM, BN>(p, b, h, q0, wave, lane, list, L::MAX_LIST, kv_len, q_len);
 
   // ---- Q fragments: B operand of S^T = K Q^T; lane (c, hh) holds Q[my_q][16 ks + 8 hh .. +7] ----
   bf16x8 qf[KS];
@@ -301,26 +265,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
   // tile j is computed. Tiles [0, n_free) need no masking for any wave of the workgroup and run a
   // body without mask code; the rest (causal diagonal, ragged tail, padded query rows) check per
   // wave whether they see the tile at all and apply the element mask.
-  int n_free;
-  if constexpr (MASK == MASK_CAUSAL) {
-    n_free = min(q0 / BN, p.seq_k / BN);
-  } else if constexpr (MASK == MASK_PADDING) {
-    n_free = (q0 + BM <= q_len) ? kv_len / BN : 0;
-  } else if constexpr (MASK == MASK_BLOCK) {
-    n_free = (n_tiles > 0 && tile_index(n_tiles - 1) * BN + BN > p.seq_k) ? n_tiles - 1 : n_tiles;
-  } else if constexpr (MASK == MASK_DENSE) {
-    n_free = 0;   // every kept tile is tested pair by pair
-  } else {
-    n_free = p.seq_k / BN;
-  }
-  n_free = min(n_free, n_tiles);
-  // split-KV: this workgroup visits tiles [t0, t1) of the item's list, an equal share of it
-  int t0 = 0, t1 = n_tiles;
-  if (p.kv_splits > 1) {
-    const int chunk = (n_tiles + p.kv_splits - 1) / p.kv_splits;
-    t0 = min(split * chunk, n_tiles);
-    t1 = min(t0 + chunk, n_tiles);
-  }
+  const int n_free =
+      fwd_free_tiles<MASK, BM, BN>(p, q0, kv_len, q_len, n_tiles, n_tiles > 0 ? tile_index(n_tiles - 1) : 0);
+  int t0, t1;
+  fwd_split_range(p, split, n_tiles, t0, t1);
   const int t_free = min(max(n_free, t0), t1);
 
   auto step = [&](auto stage_tag, auto masked_tag, int j) __attribute__((always_inline)) {

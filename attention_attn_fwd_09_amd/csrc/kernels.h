@@ -47,6 +47,8 @@ hipError_t launch_plan_pair(const PlanParams& a, const PlanParams& b, hipStream_
 int fwd_bf16_block_m(int head_dim, int mask);
 hipError_t launch_fwd_bf16(const FwdParams& p, int head_dim, int mask, hipStream_t stream);
 hipError_t launch_fwd_merge(const FwdParams& p, int head_dim, hipStream_t stream);
+int fwd_fp8_block_m();
+hipError_t launch_fwd_fp8(const FwdParams& p, int head_dim, int mask, hipStream_t stream);
 
 int fwd_f32_block_m();
 hipError_t launch_fwd_f32(const FwdParams& p, int head_dim, int mask, hipStream_t stream);

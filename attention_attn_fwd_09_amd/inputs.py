@@ -32,7 +32,7 @@ class Workload:
     """Shape and mask recipe of one attention problem."""
 
     name: str
-    dtype: str  # "f32" or "bf16"
+    dtype: str  # "f32", "bf16" or "fp8" (OCP e4m3 inputs, forward only)
     batch: int
     heads_q: int
     heads_kv: int
@@ -74,6 +74,8 @@ def _normal(shape, seed: int, dtype: str) -> torch.Tensor:
     x = torch.randn(*shape, generator=_gen(seed), dtype=torch.float32)
     if dtype == "bf16":
         x = x.to(torch.bfloat16)
+    elif dtype == "fp8":
+        x = x.to(torch.float8_e4m3fn)   # round to nearest even; N(0, 1) stays far below 448
     return x
 
 

@@ -27,6 +27,7 @@ import time
 METRIC = "attention fwd/bwd TFLOP/s (bf16) + % of MFMA peak on 1 MI355X, seq 2048-8192"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 KERNEL_NAMES = {0: "plan", 1: "fwd", 2: "bwd_pre", 3: "bwd_dkdv", 4: "bwd_dq", 5: "fwd_merge", 6: "bwd_dq_convert",
                 7: "mask_pack"}
 
@@ -345,6 +346,29 @@ def forward_all(lib, torch, dev, workloads, workload_inputs):
     split_kv_diag(lib, torch, dev)
     bwd_modes_diag(lib, torch, dev, workloads, workload_inputs)
     dense_mask_diag(lib, torch, dev)
+    fp8_diag(lib, torch, dev, workloads, workload_inputs)
+
+
+def fp8_diag(lib, torch, dev, workloads, workload_inputs):
+    """Forward with fp8 (e4m3) inputs at the causal GQA workload's shape, against the same values
+    in bf16; TFLOP/s counts 4*D flops per visible pair; the fp8 line is also given against the
+    5.0 PFLOP/s dense fp8 MFMA peak."""
+    cfg = 4
+    w = workloads[cfg]
+    inp = workload_inputs(cfg)
+    q8, k8, v8 = (inp[x].float().to(torch.float8_e4m3fn).to(dev).contiguous() for x in ("q", "k", "v"))
+    q16, k16, v16 = (x.to(torch.bfloat16) for x in (q8, k8, v8))
+    m = lib.Mask(kind=w.mask)
+    fl = 4 * w.head_dim * visible_pairs(w, inp)
+    line = {"workload": w.name.replace("bf16", "fp8")}
+    for label, (q, k, v) in (("fp8", (q8, k8, v8)), ("bf16", (q16, k16, v16))):
+        o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        med, _, _ = time_calls(torch, lambda: lib.attn_fwd(q, k, v, mask=m, scale=inp["scale"], out=o, lse=lse))
+        line[f"{label}_ms"] = round(med, 5)
+        line[f"{label}_tflops"] = round(fl / med / 1e9, 2)
+    line["fp8_pct_of_fp8_peak"] = round(100 * line["fp8_tflops"] / PEAK_FP8_TFLOPS, 2)
+    log(json.dumps(line))
 
 
 def dense_mask_diag(lib, torch, dev):

@@ -67,7 +67,10 @@ typedef enum {
   ATTN_ERR_HIP = 9          /* the HIP runtime reported an error when launching */
 } attn_status;
 
-typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
+/* Element types. ATTN_FP8_E4M3 (OCP e4m3, 1 byte) is a forward input type: Q, K, V are fp8,
+ * O is written in bf16 and LSE in fp32; a per-tensor dequantisation of the inputs folds into the
+ * arguments (scale *= q_scale * k_scale; multiply O by v_scale afterwards). */
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1, ATTN_FP8_E4M3 = 2 } attn_dtype;
 
 typedef enum {
   ATTN_MASK_NONE = 0,    /* every key visible */
@@ -123,7 +126,7 @@ size_t attn_fwd_workspace_bytes(const attn_problem *problem, const attn_mask *ma
  * Q, K, V: inputs (see layout above). O: output in the problem dtype.
  * LSE: float32 output [batch, heads_q, seq_q]. workspace: device scratch of
  * at least attn_fwd_workspace_bytes() bytes (may be NULL if that is 0).
- * Supported: dtype F32 or BF16; head_dim 64 or 128; every mask kind;
+ * Supported: dtype F32, BF16 or FP8_E4M3 (O in bf16 for fp8 inputs); head_dim 64 or 128; every mask kind;
  * heads_q a multiple of heads_kv.
  */
 attn_status attn_fwd(const attn_problem *problem, const void *Q, const void *K, const void *V,

@@ -92,7 +92,7 @@ def _fwd_ok_ptrs():
 @pytest.mark.parametrize("field,value,status", [
     ("batch", 0, B.ATTN_ERR_SHAPE), ("heads_q", 0, B.ATTN_ERR_SHAPE), ("heads_kv", 0, B.ATTN_ERR_SHAPE),
     ("seq_q", 0, B.ATTN_ERR_SHAPE), ("seq_k", -1, B.ATTN_ERR_SHAPE), ("heads_kv", 3, B.ATTN_ERR_SHAPE),
-    ("dtype", 7, B.ATTN_ERR_DTYPE), ("head_dim", 96, B.ATTN_ERR_UNSUPPORTED), ("head_dim", 256, B.ATTN_ERR_UNSUPPORTED),
+    ("dtype", 7, B.ATTN_ERR_DTYPE), ("dtype", 3, B.ATTN_ERR_DTYPE), ("head_dim", 96, B.ATTN_ERR_UNSUPPORTED), ("head_dim", 256, B.ATTN_ERR_UNSUPPORTED),
     ("seq_q", 1 << 24, B.ATTN_ERR_UNSUPPORTED),
 ])
 def test_fwd_rejects_bad_problem(field, value, status):
@@ -285,3 +285,24 @@ def test_dense_mask_arguments():
     # the mask is an input: an output overlapping it is rejected
     m.dense = ptr["o"] + 64
     assert _fwd(lib, p, m, ws=ptr["ws"], ws_bytes=need, **kw) == B.ATTN_ERR_ALIAS
+
+
+def test_fp8_inputs_arguments():
+    lib = _lib()
+    ptr = _fwd_ok_ptrs()
+    kw = dict(q=ptr["q"], k=ptr["k"], v=ptr["v"], o=ptr["o"], lse=ptr["lse"])
+    p8 = _problem(dtype=B.ATTN_FP8_E4M3, sq=64, sk=64, d=128)
+    # accepted by the forward (workspace only for masks that plan); the output is bf16-sized
+    assert lib.attn_fwd_workspace_bytes(ctypes.byref(p8), ctypes.byref(_mask())) == 0
+    assert lib.attn_fwd_workspace_bytes(ctypes.byref(p8), ctypes.byref(_mask(kind=3, layout=FAKE))) > 0
+    # O of 2 x 64 x 128 bf16 = 32 KiB: an O placed 16 KiB below Q overlaps it, although an fp8-sized O would not
+    q = ptr["q"]
+    assert _fwd(lib, p8, _mask(), q=q, k=kw["k"], v=kw["v"], o=q - 16384, lse=kw["lse"]) == B.ATTN_ERR_ALIAS
+    # split-KV accepts fp8; the backward does not
+    assert lib.attn_fwd_kv_splits(ctypes.byref(p8), ctypes.byref(_mask()), 2) == 1   # one 64-key tile
+    p8_long = _problem(dtype=B.ATTN_FP8_E4M3, sq=64, sk=4096, d=128)
+    assert lib.attn_fwd_kv_splits(ctypes.byref(p8_long), ctypes.byref(_mask()), 4) == 4
+    qq, k, v, o, do, lse, dq, dk, dv, ws = _spaced(10)
+    assert lib.attn_bwd(ctypes.byref(p8), qq, k, v, o, do, lse, ctypes.byref(_mask()), 0.1, dq, dk, dv, ws, 1 << 30,
+                        None) == B.ATTN_ERR_UNSUPPORTED
+    assert _fwd(lib, _problem(dtype=3), _mask(), **kw) == B.ATTN_ERR_DTYPE
