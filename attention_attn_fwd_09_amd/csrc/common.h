@@ -44,6 +44,9 @@ __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" 
 // where two rows share one 256-byte bank span) follow the row's position inside its group of 4,
 // and its low bits separate the four 4-row groups of a row-fragment read. Writes fill one row's
 // chunks per 16 lanes, which any per-row XOR permutes without conflict.
+// ds_read_b64_tr_b16 works on 16-lane groups: the 4 rows of one read are each assembled from 4
+// lanes' 8-byte pieces (lanes 4r..4r+3 supply row r) and lane i receives element i of every row,
+// so two reads give a lane 8 consecutive rows of one column (an MFMA operand along the rows).
 template <int D> __device__ __forceinline__ int swz(int row);
 template <> __device__ __forceinline__ int swz<128>(int row) {
   return ((row & 3) << 2) | ((row >> 2) & 1) | ((row >> 3) & 2);
@@ -66,54 +69,6 @@ __device__ __forceinline__ void issue_rows(char* lds_tile, __amdgpu_buffer_rsrc_
     const int pc = pos % CPR;
     buffer_to_lds16(r, lds_tile + blk * 1024, (uint32_t)(row0 + row) * (D * 2) + (uint32_t)((pc ^ swz<D>(row)) * 16));
   }
-}
-
-// Register-staged variant of issue_rows: each thread loads its chunks of the 64-row tile into
-// VGPRs (load_rows) and later writes them to LDS (store_rows) at the same swizzled positions.
-template <int D, int NW>
-struct RowStage {
-  static constexpr int N = (64 * (D / 8)) / (NW * 64);
-  i32x4 v[N];
-};
-template <int D, int NW>
-__device__ __forceinline__ void load_rows(RowStage<D, NW>& st, __amdgpu_buffer_rsrc_t r, int row0, int tid) {
-  constexpr int CPR = D / 8;
-#pragma unroll
-  for (int it = 0; it < RowStage<D, NW>::N; ++it) {
-    const int pos = it * (NW * 64) + tid;
-    const int row = pos / CPR, pc = pos % CPR;
-    st.v[it] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
-        r, (uint32_t)(row0 + row) * (D * 2) + (uint32_t)((pc ^ swz<D>(row)) * 16), 0, 0));
-  }
-}
-template <int D, int NW>
-__device__ __forceinline__ void store_rows(char* lds_tile, const RowStage<D, NW>& st, int tid) {
-#pragma unroll
-  for (int it = 0; it < RowStage<D, NW>::N; ++it) *(i32x4*)(lds_tile + (it * (NW * 64) + tid) * 16) = st.v[it];
-}
-
-// Row fragment: 8 bf16 of logical chunk `chunk` of tile row `row`.
-template <int D>
-__device__ __forceinline__ bf16x8 lds_row_frag(const char* tile, int row, int chunk) {
-  return *(const bf16x8*)(tile + row * (D * 2) + ((chunk ^ swz<D>(row)) * 16));
-}
-
-// Transposed fragment: an MFMA operand whose lane holds 8 consecutive tile rows at one column.
-// row0 is the first of those 8 rows for the calling lane's half-wave, dbase the column of the
-// first lane of its 16-lane group, i16 = lane & 15; the lane receives column dbase + i16 of rows
-// row0 .. row0+7. ds_read_b64_tr_b16 works on 16-lane groups: the 4 rows of one read are each
-// assembled from 4 lanes' 8-byte pieces (lanes 4r..4r+3 supply row r) and lane i16 receives
-// element i16 of every row, so lane i16 addresses row row0 + i16/4, columns dbase + 4*(i16%4)..+3.
-template <int D>
-__device__ __forceinline__ bf16x8 lds_tr_frag(const char* tile, int row0, int dbase, int i16) {
-  const int r0 = row0 + (i16 >> 2);
-  const int r1 = r0 + 4;
-  const int d = dbase + 4 * (i16 & 3);
-  const char* p0 = tile + r0 * (D * 2) + (((d >> 3) ^ swz<D>(r0)) * 16) + (d & 7) * 2;
-  const char* p1 = tile + r1 * (D * 2) + (((d >> 3) ^ swz<D>(r1)) * 16) + (d & 7) * 2;
-  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, p0));
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, p1));
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
