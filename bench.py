@@ -309,12 +309,18 @@ def cpu_baseline(w, inp, pairs_total):
             "seconds": round(secs, 2)}
 
 
-def time_calls(torch, fn, n=20, warm=10):
-    """Median, min and mean milliseconds of n calls of fn after warm untimed calls (one event pair
-    per call on the current stream)."""
+def time_calls(torch, fn, n=20, warm=10, settle_s=0.2):
+    """Median, min and mean milliseconds of n calls of fn after warm untimed calls and at least
+    settle_s seconds of untimed calls (so that the clocks have left their idle state); one event
+    pair per call on the current stream."""
     for _ in range(warm):
         fn()
     torch.cuda.synchronize()
+    t_end = time.perf_counter() + settle_s
+    while time.perf_counter() < t_end:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
     for a, b in ev:
         a.record()
@@ -448,8 +454,10 @@ def split_kv_diag(lib, torch, dev):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # The GPU's clocks settle within about 50 ms of sustained work (about 100 steps): the default
+    # warmup covers that, and the timed steps then measure the steady-state rate (about 0.4 s).
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all", action="store_true", help="also print forward timings of every workload to stderr")
     ap.add_argument("--copy-mib", type=int, default=0,
