@@ -10,6 +10,9 @@ Prints one JSON line. `value` is algorithmic TFLOP/s: 4*D flops per visible (que
 the forward plus 10*D for the backward (five products); masked and skipped work is not counted.
 `roofline` describes the dominant kernel, timed live with HIP events on the library's stream;
 `cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same workload.
+Secondary figures, measured after the timed region: `cold_cache` (the same step with 512 MiB
+written before each one, so that the inputs come from HBM) and `gfx_clock` (the graphics clock
+amdsmi reports while the step runs, giving `pct_of_clock_adjusted_bf16_peak`).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--all]
 """
@@ -255,6 +258,16 @@ def run_gpu(args):
         "roofline": roofline,
         "kernels_ms_per_step": {KERNEL_NAMES[c]: round(per_class[c][0], 5) for c in per_class},
     }
+    # secondary figures, measured after the timed region: the same step with cold caches, and the
+    # graphics clock the step runs at (for the clock-adjusted peak)
+    cold = cold_cache_steps(torch, step, stream)
+    cold["value"] = round(flops_step / (cold["ms_per_step_median"] * 1e-3) / 1e12, 2)
+    result["cold_cache"] = cold
+    clk = gfx_clock_under_load(torch, step)
+    result["gfx_clock"] = clk
+    if clk is not None:
+        adj = PEAK_BF16_TFLOPS * clk["mhz_median"] / 2400.0
+        result["pct_of_clock_adjusted_bf16_peak"] = round(100 * tflops / adj, 2)
     sample = None
     if not args.no_cpu_baseline:
         sample = cpu_baseline(w, inp, pairs)
@@ -273,6 +286,70 @@ def run_gpu(args):
         torch.cuda.synchronize()
         result["copy_calibration_bytes"] = n
     return result
+
+
+def gfx_clock_under_load(torch, step, seconds=1.5, skip_s=0.5):
+    """Median graphics clock (MHz) that amdsmi reports while `step` runs back to back for
+    `seconds` (samples of the first `skip_s` seconds dropped); None when amdsmi is unavailable.
+    The driver refreshes the value about once a second, so this runs outside the timed region."""
+    import threading
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        handle = amdsmi.amdsmi_get_processor_handles()[torch.cuda.current_device()]
+    except Exception as e:  # telemetry only: the measurement itself does not depend on it
+        log(f"amdsmi unavailable ({e}); no clock reading")
+        return None
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        t0 = time.perf_counter()
+        while not stop.is_set():
+            try:
+                mhz = amdsmi.amdsmi_get_gpu_metrics_info(handle).get("current_gfxclk")
+            except Exception:
+                mhz = None
+            if isinstance(mhz, (int, float)) and time.perf_counter() - t0 >= skip_s:
+                samples.append(float(mhz))
+            time.sleep(0.02)
+
+    th = threading.Thread(target=sampler)
+    th.start()
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    try:
+        amdsmi.amdsmi_shut_down()
+    except Exception:
+        pass
+    if not samples:
+        return None
+    samples.sort()
+    return {"mhz_median": samples[len(samples) // 2], "mhz_min": samples[0], "mhz_max": samples[-1],
+            "samples": len(samples), "source": "amdsmi current_gfxclk, untimed run of the same step"}
+
+
+def cold_cache_steps(torch, step, stream, n=20, flush_mib=512):
+    """Mean ms of `n` steps, each preceded (outside its event pair) by a 512 MiB write that
+    evicts the inputs from L2 and the 256 MiB Infinity Cache."""
+    buf = torch.empty(flush_mib << 20, dtype=torch.uint8, device="cuda")
+    ms = []
+    for i in range(n):
+        buf.fill_(i & 255)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+    del buf
+    ms.sort()
+    return {"ms_per_step_median": round(ms[len(ms) // 2], 5), "ms_per_step_min": round(ms[0], 5), "steps": n,
+            "flush_mib": flush_mib}
 
 
 def cpu_baseline(w, inp, pairs_total):
