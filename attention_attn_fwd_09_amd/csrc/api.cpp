@@ -555,15 +555,22 @@ attn_status attn_bwd_ex(const attn_problem* problem, const void* Q, const void* 
     st = hip_status(timed(ATTN_KERNEL_PLAN, s, [&] { return launch_plan_pair(pk, pq, s); }));
   if (st != ATTN_OK) return st;
 
-  st = hip_status(timed(ATTN_KERNEL_BWD_PRE, s, [&] { return launch_bwd_preprocess(bp, p->head_dim, s); }));
-  if (st != ATTN_OK) return st;
-  st = hip_status(timed(ATTN_KERNEL_BWD_DKDV, s,
-                        [&] { return launch_bwd_dkdv(bp, p->head_dim, m->kind, (int)bs.kv_items, s); }));
-  if (st != ATTN_OK) return st;
-  if (atomic_dq)
+  if (atomic_dq) {
+    // single pass: the preprocess writes the row statistics and zeroes the dQ accumulator
+    st = hip_status(timed(ATTN_KERNEL_BWD_PRE, s, [&] { return launch_bwd_preprocess(bp, p->head_dim, s); }));
+    if (st != ATTN_OK) return st;
+    st = hip_status(timed(ATTN_KERNEL_BWD_DKDV, s,
+                          [&] { return launch_bwd_dkdv(bp, p->head_dim, m->kind, (int)bs.kv_items, s); }));
+    if (st != ATTN_OK) return st;
     return hip_status(timed(ATTN_KERNEL_BWD_DQ_CONVERT, s, [&] { return launch_bwd_dq_convert(bp, p->head_dim, s); }));
-  return hip_status(
+  }
+  // two passes: the dQ pass computes the row statistics (-Delta, LSE*log2(e)) of its queries as it
+  // starts and writes them for the dK/dV pass, so it runs first and no preprocess is launched
+  st = hip_status(
       timed(ATTN_KERNEL_BWD_DQ, s, [&] { return launch_bwd_dq(bp, p->head_dim, m->kind, (int)bs.q_items, s); }));
+  if (st != ATTN_OK) return st;
+  return hip_status(timed(ATTN_KERNEL_BWD_DKDV, s,
+                          [&] { return launch_bwd_dkdv(bp, p->head_dim, m->kind, (int)bs.kv_items, s); }));
 }
 
 }  // extern "C"

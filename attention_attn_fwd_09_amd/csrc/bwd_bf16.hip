@@ -8,15 +8,18 @@
 // and must resolve write conflicts. This file takes the two-loop option (no output atomics, a
 // deterministic result):
 //
-//   preprocess  Delta_i = sum_d dO_id O_id (equal to sum_j P_ij dP_ij; fp32, one value per row,
-//               stored negated so that it can seed the dP accumulators)
+//   dQ pass     (runs first) one workgroup per query tile: Q_i, dO_i stay in registers; the
+//               workgroup first computes its rows' Delta_i = sum_d dO_id O_id (equal to
+//               sum_j P_ij dP_ij; fp32, stored negated so that it can seed the dP accumulators)
+//               and LSE_i log2(e), and writes both for the next pass; then the visible key tiles
+//               stream through LDS, S, P, dP, dS are recomputed and dQ_i += scale dS K_j.
 //   dK/dV pass  one workgroup per key tile: K_j, V_j stay in registers, every (query head of the
 //               group, query tile) that sees the tile streams Q_i, dO_i, LSE_i, Delta_i through
 //               LDS; S = Q_i K_j^T and dP = dO_i V_j^T are recomputed, P = exp(scale S - LSE),
 //               dS = P (dP - Delta), and dV_j += P^T dO_i, dK_j += scale dS^T Q_i accumulate in
 //               registers.
-//   dQ pass     one workgroup per query tile: Q_i, dO_i stay in registers, the visible key tiles
-//               stream through LDS, S, P, dP, dS are recomputed and dQ_i += scale dS K_j.
+//   preprocess  the same row statistics as a kernel of their own, for the single-pass variant
+//               (which has no dQ pass).
 //
 // Skipped blocks of a block-sparse layout (and fully masked causal/padding tiles) are never
 // visited. Every product runs on v_mfma_f32_32x32x16_bf16; operands that must be read along the
@@ -39,29 +42,35 @@ constexpr float LOG2E = 1.4426950408889634f;
 __device__ __forceinline__ float lse_to_log2(float l) { return l == -INFINITY ? INFINITY : l * LOG2E; }
 
 // ------------------------------------------------------------------------------------------------
-// Preprocess: -Delta = -rowsum(dO * O), one group of D/8 lanes per row (16 bytes per lane), and
-// the row's LSE in the log2 domain (so the two passes subtract it without converting per element).
+// Preprocess of the single-pass variant: -Delta = -rowsum(dO * O) and the row's LSE in the log2
+// domain (so the passes subtract it without converting per element). Two lanes per row, summing
+// in the order the dQ pass uses for the same statistics (lane half h: columns 16 ks + 8 h + e in
+// order, then the two halves added), so both variants see bit-identical -Delta.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int64_t rows) {
-  constexpr int LPR = D / 8;
-  const int64_t row = (int64_t)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
-  const int sub = threadIdx.x % LPR;
+  constexpr int KS = D / 16;
+  const int64_t row = (int64_t)blockIdx.x * 128 + threadIdx.x / 2;
+  const int half = threadIdx.x & 1;
   float acc = 0.0f;
   if (row < rows) {
-    const bf16x8 o = *((const bf16x8*)((const bf16*)p.o + row * D) + sub);
-    const bf16x8 g = *((const bf16x8*)((const bf16*)p.dout + row * D) + sub);
+    const bf16* o = (const bf16*)p.o + row * D + half * 8;
+    const bf16* g = (const bf16*)p.dout + row * D + half * 8;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc = fmaf((float)o[e], (float)g[e], acc);
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 o8 = *(const bf16x8*)(o + ks * 16);
+      const bf16x8 g8 = *(const bf16x8*)(g + ks * 16);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc = fmaf((float)o8[e], (float)g8[e], acc);
+    }
   }
-#pragma unroll
-  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
+  acc += __shfl_xor(acc, 1, 2);
   if (p.dq_acc != nullptr && row < rows) {
-    // single-pass mode: this row's slice of the dQ accumulator starts at zero
-    float* z = p.dq_acc + row * D + sub * 8;
-    *(f32x4*)z = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    *(f32x4*)(z + 4) = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    // single-pass mode: this row's half of the dQ accumulator starts at zero
+    float* z = p.dq_acc + row * D + half * (D / 2);
+#pragma unroll
+    for (int i = 0; i < D / 2; i += 4) *(f32x4*)(z + i) = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
-  if (row < rows && sub == 0) {
+  if (row < rows && half == 0) {
     p.delta[row] = -acc;
     p.lse2[row] = lse_to_log2(p.lse[row]);
   }
@@ -170,7 +179,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdParams p) {
       }
       if (lane == 0) list_count = min(count, L::MAX_STEPS);
     }
-    __syncthreads();
+    lds_barrier();   // the K and V loads issued above stay in flight
     n_steps = list_count;
     // ragged shapes run every step through the masked body, and so does a dense mask
     n_free = (MASK == MASK_DENSE || key_tail || (p.seq_q % BQ) != 0) ? 0 : n_steps;
@@ -597,6 +606,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
   const __amdgpu_buffer_rsrc_t rdo = make_rsrc((const bf16*)p.dout + q_off, (uint32_t)p.seq_q * RB);
   const __amdgpu_buffer_rsrc_t rk = make_rsrc((const bf16*)p.k + kv_off, (uint32_t)p.seq_k * RB);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc((const bf16*)p.v + kv_off, (uint32_t)p.seq_k * RB);
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc((const bf16*)p.o + q_off, (uint32_t)p.seq_q * RB);
+
+  // Q and dO rows of this lane's query (B operands of S^T = K Q^T and dP^T = V dO^T), and its O
+  // row for the row statistics below; issued before the key-tile list so that they overlap it
+  bf16x8 qf[KS], dof[KS], of8[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const uint32_t off = (uint32_t)my_q * RB + (uint32_t)(ks * 32 + hh * 16);
+    qf[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
+    dof[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rdo, off, 0, 0));
+    of8[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0, 0));
+  }
 
   int kv_len = p.seq_k, q_len = p.seq_q;
   int n_tiles;
@@ -629,26 +650,34 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
       }
       if (lane == 0) list[L::MAX_LIST] = (uint32_t)count;
     }
-    __syncthreads();
+    lds_barrier();   // the row loads issued above stay in flight
     n_tiles = (int)list[L::MAX_LIST];
   } else {
     n_tiles = (p.seq_k + BN - 1) / BN;
   }
 
-  // Q and dO rows of this lane's query (B operands of S^T = K Q^T and dP^T = V dO^T)
-  bf16x8 qf[KS], dof[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const uint32_t off = (uint32_t)my_q * RB + (uint32_t)(ks * 32 + hh * 16);
-    qf[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
-    dof[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rdo, off, 0, 0));
-  }
   const size_t row_off = (size_t)(b * p.heads_q + h) * p.seq_q;
   const uint32_t* dense_row = MASK == MASK_DENSE
       ? p.dense.rows + b * p.dense.rows_stride_b + h * p.dense.rows_stride_h + (int64_t)my_q * p.dense.row_words
       : nullptr;
-  const float lse2 = my_q < p.seq_q ? p.lse2[row_off + my_q] : INFINITY;
-  const float ndelta = my_q < p.seq_q ? p.delta[row_off + my_q] : 0.0f;   // -Delta
+  // The backward's row statistics of this workgroup's queries, computed here rather than by a
+  // preprocess kernel: -Delta = -rowsum(dO * O) in fp32 (the lane and its partner lane c + 32 hold
+  // the two halves of the row) and LSE in the log2 domain. The dK/dV pass, launched after this
+  // one, reads them from the workspace.
+  float dsum = 0.0f;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dsum = fmaf((float)of8[ks][e], (float)dof[ks][e], dsum);
+  }
+  dsum = partner_sum(dsum);
+  const bool row_ok = my_q < p.seq_q;
+  const float lse2 = row_ok ? lse_to_log2(p.lse[row_off + my_q]) : INFINITY;
+  const float ndelta = row_ok ? -dsum : 0.0f;   // -Delta
+  if (row_ok && hh == 0) {
+    p.delta[row_off + my_q] = ndelta;
+    p.lse2[row_off + my_q] = lse2;
+  }
 
   // per-lane LDS offsets: row fragments (K and V tiles share the layout) and transposed K reads
   int roff[KS];
@@ -882,8 +911,7 @@ int bwd_max_steps() { return KvLds<128>::MAX_STEPS; }
 
 hipError_t launch_bwd_preprocess(const BwdParams& p, int head_dim, hipStream_t s) {
   const int64_t rows = (int64_t)p.batch * p.heads_q * p.seq_q;
-  const int rpb = 256 / (head_dim / 8);
-  const unsigned grid = (unsigned)((rows + rpb - 1) / rpb);
+  const unsigned grid = (unsigned)((rows + 127) / 128);   // two lanes per row
   if (head_dim == 128)
     hipLaunchKernelGGL(bwd_pre_kernel<128>, dim3(grid), dim3(256), 0, s, p, rows);
   else

@@ -33,6 +33,14 @@ __device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t r, void* 
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Workgroup barrier that publishes LDS writes only: this wave's LDS operations complete, then
+// s_barrier. Unlike __syncthreads it does not wait for outstanding global loads, so loads issued
+// before it (a workgroup's row fragments) stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt fields at their maximum
+  asm volatile("s_barrier" ::: "memory");
+}
+
 // --- LDS tiles: 64 rows x D bf16, rows of D*2 bytes, 16-byte chunks XOR-swizzled per row ---
 // LDS serves 256 bytes per clock from 64 four-byte banks; a 16-byte chunk's bank group is
 // (byte offset / 16) mod 16. Tiles are read in two patterns:

@@ -87,10 +87,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
   const __amdgpu_buffer_rsrc_t rk = make_rsrc((const bf16*)p.k + kv_off, (uint32_t)p.seq_k * RB);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc((const bf16*)p.v + kv_off, (uint32_t)p.seq_k * RB);
 
-  // ---- key tiles this item walks ----
-  int kv_len, q_len;
-  const int n_tiles = fwd_key_tiles<MASK, BM, BN>(p, b, h, q0, wave, lane, list, L::MAX_LIST, kv_len, q_len);
-
   // ---- Q fragments: B operand of S^T = K Q^T; lane (c, hh) holds Q[my_q][16 ks + 8 hh .. +7] ----
   bf16x8 qf[KS];
 #pragma unroll
@@ -99,6 +95,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
         rq, (uint32_t)my_q * RB + (uint32_t)(ks * 32 + hh * 16), 0, 0));
     qf[ks] = __builtin_bit_cast(bf16x8, raw);
   }
+
+  // ---- key tiles this item walks ----
+  int kv_len, q_len;
+  const int n_tiles = fwd_key_tiles<MASK, BM, BN>(p, b, h, q0, wave, lane, list, L::MAX_LIST, kv_len, q_len);
 
   // ---- per-lane LDS byte offsets inside a tile; everything else in an address is a constant ----
   // K row fragment for k-step ks of key block kb: koff[ks] + kb * 32 rows.

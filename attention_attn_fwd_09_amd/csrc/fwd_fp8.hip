@@ -114,9 +114,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
   const __amdgpu_buffer_rsrc_t rk = make_rsrc((const uint8_t*)p.k + kv_off, (uint32_t)p.seq_k * RB);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc((const uint8_t*)p.v + kv_off, (uint32_t)p.seq_k * RB);
 
-  int kv_len, q_len;
-  const int n_tiles = fwd_key_tiles<MASK, BM, BN>(p, b, h, q0, wave, lane, list, L::MAX_LIST, kv_len, q_len);
-
   // Q fragments (B operand of S^T = K Q^T): lane (c, hh) holds Q[my_q][ks*64 + hh*32 + 0..31]
   i32x8 qf[KS];
 #pragma unroll
@@ -126,6 +123,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
     const i32x4 hi = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, off + 16, 0, 0));
     qf[ks] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   }
+  int kv_len, q_len;
+  const int n_tiles = fwd_key_tiles<MASK, BM, BN>(p, b, h, q0, wave, lane, list, L::MAX_LIST, kv_len, q_len);
+
   // per-lane LDS offsets: K row fragment of k-step ks, chunk half j (key block kb adds 32 rows)
   int koff[KS][2];
 #pragma unroll

@@ -50,7 +50,7 @@ __device__ __forceinline__ int fwd_key_tiles(const FwdParams& p, int b, int h, i
       }
       if (lane == 0) list[max_list] = (uint32_t)count;
     }
-    __syncthreads();
+    lds_barrier();   // the Q loads issued before the list stay in flight
     return (int)list[max_list];
   } else {
     return (p.seq_k + BN - 1) / BN;

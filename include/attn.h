@@ -207,7 +207,8 @@ size_t attn_bwd_ex_workspace_bytes(const attn_problem *problem, const attn_mask 
 typedef enum {
   ATTN_KERNEL_PLAN = 0,     /* tile-list scheduler */
   ATTN_KERNEL_FWD = 1,      /* fused forward */
-  ATTN_KERNEL_BWD_PRE = 2,  /* backward preprocess, Delta = rowsum(dO * O) */
+  ATTN_KERNEL_BWD_PRE = 2,  /* backward preprocess, Delta = rowsum(dO * O) (single-pass mode only;
+                               the two-pass dQ pass computes it for its own rows) */
   ATTN_KERNEL_BWD_DKDV = 3, /* backward dK/dV pass */
   ATTN_KERNEL_BWD_DQ = 4,   /* backward dQ pass */
   ATTN_KERNEL_FWD_MERGE = 5, /* split-KV merge of the forward */
