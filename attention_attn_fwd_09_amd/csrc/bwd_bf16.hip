@@ -248,11 +248,16 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdParams p) {
     }
   }
 
-  // dense mask: bits of queries q0 + qb*32 .. +31 for this lane's key (0 past the key range)
-  auto dcol_word = [&](const uint32_t* dcol, int q0, int qb) __attribute__((always_inline)) -> uint32_t {
-    const int w = (q0 + qb * 32) >> 5;
-    return (my_k < p.seq_k && w < p.dense.col_words) ? dcol[w] : 0u;
+  // dense mask: bits of the step's queries q0 .. q0+63 for this lane's key and the step's query
+  // head (0 past the key range), two words; loaded one step ahead of the step that tests them
+  auto dcol_words = [&](int s, uint32_t (&w)[2]) __attribute__((always_inline)) {
+    int g, qt;
+    step_at(s, g, qt);
+    const uint32_t* dcol = p.dense.cols + b * p.dense.cols_stride_b + (kvh * p.group + g) * p.dense.cols_stride_h +
+                           (int64_t)min(my_k, p.seq_k - 1) * p.dense.col_words;
+    dense_words(dcol, my_k < p.seq_k, p.dense.col_words, qt * BQ, w);
   };
+  uint32_t dcur[2] = {0u, 0u}, dnext[2] = {0u, 0u};
 
   f32x16 dk[DB], dv[DB];
 #pragma unroll
@@ -267,7 +272,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdParams p) {
   // P = exp2(scale log2(e) S - LSE log2(e)) and dS = P (dP - Delta), then dV += P^T dO and
   // dK += dS^T Q. The two blocks are software-pipelined so that the vector work of one block runs
   // under the MFMAs of the other: [S,dP 0] [S,dP 1 | P,dS 0] [dV,dK 0 | P,dS 1] [dV,dK 1].
-  auto body = [&](auto stage_tag, auto masked_tag, int q0, const uint32_t* dcol) __attribute__((always_inline)) {
+  auto body = [&](auto stage_tag, auto masked_tag, int q0) __attribute__((always_inline)) {
     constexpr int ST = decltype(stage_tag)::value;
     constexpr bool MASKED = decltype(masked_tag)::value;
     const char* ql = ST == 0 ? q_st0 : q_st1;
@@ -331,7 +336,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdParams p) {
           const int q = q0 + qb * 32 + hh * 16 + i;
           bool vis = q < q_len && my_k < kv_len;
           if constexpr (MASK == MASK_CAUSAL) vis = vis && my_k <= q;
-          if constexpr (MASK == MASK_DENSE) vis = vis && ((dcol_word(dcol, q0, qb) >> (hh * 16 + i)) & 1u);
+          if constexpr (MASK == MASK_DENSE) vis = vis && ((dcur[qb] >> (hh * 16 + i)) & 1u);
           pv = vis ? pv : 0.0f;
         }
         pb[i >> 3][i & 7] = (bf16)pv;
@@ -415,7 +420,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdParams p) {
 
   // One step of the single-pass variant, one 32-query block at a time: the two-pass body's
   // products, then dQ_i += dS K_j for this wave's 32 keys, added to the fp32 accumulator.
-  auto body_atomic = [&](auto stage_tag, auto masked_tag, int q0, int hq, const uint32_t* dcol)
+  auto body_atomic = [&](auto stage_tag, auto masked_tag, int q0, int hq)
                          __attribute__((always_inline)) {
     constexpr int ST = decltype(stage_tag)::value;
     constexpr bool MASKED = decltype(masked_tag)::value;
@@ -452,7 +457,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdParams p) {
           const int q = q0 + qbase + i;
           bool vis = q < q_len && my_k < kv_len;
           if constexpr (MASK == MASK_CAUSAL) vis = vis && my_k <= q;
-          if constexpr (MASK == MASK_DENSE) vis = vis && ((dcol_word(dcol, q0, qb) >> (hh * 16 + i)) & 1u);
+          if constexpr (MASK == MASK_DENSE) vis = vis && ((dcur[qb] >> (hh * 16 + i)) & 1u);
           pv = vis ? pv : 0.0f;
         }
         pb[i >> 3][i & 7] = (bf16)pv;
@@ -517,14 +522,14 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdParams p) {
     int g, qt;
     step_at(s, g, qt);
     const int q0 = qt * BQ;
-    // dense mask: the column of bits of this lane's key for the step's query head
-    const uint32_t* dcol = MASK == MASK_DENSE
-        ? p.dense.cols + b * p.dense.cols_stride_b + (kvh * p.group + g) * p.dense.cols_stride_h +
-              (int64_t)min(my_k, p.seq_k - 1) * p.dense.col_words
-        : nullptr;
+    if constexpr (MASK == MASK_DENSE) {
+      dcur[0] = dnext[0];
+      dcur[1] = dnext[1];
+      if (s + 1 < n_steps) dcol_words(s + 1, dnext);
+    }
     auto run_body = [&]() __attribute__((always_inline)) {
-      if constexpr (ATOMIC_DQ) body_atomic(stage_tag, masked_tag, q0, kvh * p.group + g, dcol);
-      else body(stage_tag, masked_tag, q0, dcol);
+      if constexpr (ATOMIC_DQ) body_atomic(stage_tag, masked_tag, q0, kvh * p.group + g);
+      else body(stage_tag, masked_tag, q0);
     };
     if constexpr (!MASKED) {
       run_body();
@@ -545,6 +550,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdParams p) {
     if (s < s1) step(std::integral_constant<int, 0>{}, masked_tag, s);
   };
 
+  if constexpr (MASK == MASK_DENSE)
+    if (n_steps > 0) dcol_words(0, dnext);
   if (n_steps > 0) issue_step(std::integral_constant<int, 0>{}, 0);
   run(std::false_type{}, 0, n_free);
   run(std::true_type{}, n_free, n_steps);
@@ -720,7 +727,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
     for (int kb = 0; kb < 2; ++kb) {
       f32x16 sc = f32x16{}, dp = f32x16{};
       bf16x8 ka[KS], va[KS];
-      // dense mask: the query's bits for keys k0 + kb*32 .. +31
       uint32_t dw = 0;
       if constexpr (MASK == MASK_DENSE) {
         const int w = (k0 >> 5) + kb;
