@@ -31,6 +31,7 @@ namespace {
 
 constexpr int BN = 64;           // keys per tile
 constexpr float RESCALE_SLACK = 8.0f;  // log2 headroom before the reference maximum is re-based
+constexpr int K_LEAD = 4;        // k-steps of K fragment reads in flight ahead of the score MFMAs
 
 template <int D>
 struct FwdLds {
@@ -55,6 +56,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
   __shared__ __attribute__((aligned(16))) char v_st1[L::TILE_BYTES];
   // block and dense masks walk a list of kept key tiles (a dense mask through its derived layout)
   constexpr bool LISTED = MASK == MASK_BLOCK || MASK == MASK_DENSE;
+  // Structured masks issue the copy of the next tile after the score MFMAs, so that its LDS writes
+  // land while the softmax runs instead of during the burst of K reads that opens every tile (the
+  // listed masks, whose kept tiles are farther apart in memory, keep the copy at the step's start).
+  constexpr bool LATE = !LISTED;
   __shared__ uint32_t list[LISTED ? L::MAX_LIST + 1 : 1];
 
   const int tid = threadIdx.x;
@@ -139,11 +144,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
     issue_rows<D, NW>(ST == 0 ? v_st0 : v_st1, rv, kt * BN, wave, lane);
   };
 
-  // One 64-key tile for this wave's 32 queries, read from LDS stage ST. The instruction order is
+  // One 64-key tile for this wave's 32 queries, read from LDS stage ST; after_scores() runs once
+  // the score MFMAs are issued (the late copy of the next tile, or nothing). The instruction order is
   // pinned with sched_group_barrier (masks: 0x008 MFMA, 0x100 LDS read, 0x002 VALU) so that LDS
-  // reads run two k-steps ahead of the MFMAs that consume them, and the first V fragments are in
+  // reads run K_LEAD k-steps ahead of the MFMAs that consume them, and the first V fragments are in
   // flight while the softmax runs on the vector ALU.
-  auto tile = [&](auto stage_tag, auto masked_tag, int k0) __attribute__((always_inline)) {
+  auto tile = [&](auto stage_tag, auto masked_tag, int k0, auto&& after_scores) __attribute__((always_inline)) {
     constexpr int ST = decltype(stage_tag)::value;
     constexpr bool MASKED = decltype(masked_tag)::value;
     const char* kl = ST == 0 ? k_st0 : k_st1;
@@ -162,13 +168,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
       s0 = mfma32(ka[ks], qf[ks], s0);
       s1 = mfma32(kb1[ks], qf[ks], s1);
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    constexpr int KL = K_LEAD < KS ? K_LEAD : KS;
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * KL, 0);
 #pragma unroll
-    for (int ks = 0; ks < KS - 2; ++ks) {
+    for (int ks = 0; ks < KS - KL; ++ks) {
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * KL, 0);
+    if constexpr (LATE) __builtin_amdgcn_sched_barrier(0);
+    after_scores();
+    if constexpr (LATE) __builtin_amdgcn_sched_barrier(0);
 
     // ---- mask (boundary tiles only): hidden scores become -inf ----
     uint32_t dw0 = 0, dw1 = 0;   // dense mask: the query's bits for keys k0 .. k0+31, k0+32 .. k0+63
@@ -276,19 +286,24 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
     constexpr bool MASKED = decltype(masked_tag)::value;
     wait_vmem();
     __syncthreads();  // tile j is in LDS; every wave is done with the stage tile j+1 will overwrite
-    if (j + 1 < t1) issue_tile(std::integral_constant<int, 1 - ST>{}, tile_index(j + 1));
+    auto issue_next = [&]() __attribute__((always_inline)) {
+      if (j + 1 < t1) issue_tile(std::integral_constant<int, 1 - ST>{}, tile_index(j + 1));
+    };
+    if constexpr (!LATE) issue_next();
     const int k0 = tile_index(j) * BN;
-    if constexpr (!MASKED) {
-      bool active = true;
-      if constexpr (LISTED && BM > 64) active = ((list[j] >> 16) >> ((wave * 32) / 64)) & 1u;
-      if (active) tile(stage_tag, masked_tag, k0);
-    } else {
-      // wave-uniform: does this wave see any key of the tile?
-      bool active = k0 < kv_len;
+    // wave-uniform: does this wave see any key of the tile?
+    bool active = true;
+    if constexpr (LISTED && (MASKED || BM > 64)) active = ((list[j] >> 16) >> ((wave * 32) / 64)) & 1u;
+    if constexpr (MASKED && !LISTED) {
+      active = k0 < kv_len;
       if constexpr (MASK == MASK_CAUSAL) active = active && k0 <= qw0 + 31;
       if constexpr (MASK == MASK_PADDING) active = active && qw0 < q_len;
-      if constexpr (LISTED) active = ((list[j] >> 16) >> ((wave * 32) / 64)) & 1u;
-      if (active) tile(stage_tag, masked_tag, k0);
+    }
+    if constexpr (LATE) {
+      if (active) tile(stage_tag, masked_tag, k0, issue_next);
+      else issue_next();
+    } else if (active) {
+      tile(stage_tag, masked_tag, k0, [] {});
     }
   };
   auto run = [&](auto masked_tag, int j0, int j1) __attribute__((always_inline)) {
