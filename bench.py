@@ -432,6 +432,34 @@ def forward_all(lib, torch, dev, workloads, workload_inputs):
     fp8_diag(lib, torch, dev, workloads, workload_inputs)
 
 
+def forward_only(cfg: int, calls: int, warmup: int) -> dict:
+    """Forward of one workload only (the same inputs and launch as the bench's workloads), timed
+    over `calls` calls after `warmup` calls and 0.2 s of settling: one HIP event pair per call on
+    the current stream, median and mean reported, TFLOP/s on visible pairs (4*D flops each)."""
+    import torch
+
+    from attention_attn_fwd_09_amd import binding as lib
+    from attention_attn_fwd_09_amd.inputs import WORKLOADS, workload_inputs
+
+    w = WORKLOADS[cfg]
+    if w.dtype != "bf16":
+        raise SystemExit(f"--fwd-only takes a bf16 workload (2-5), not {cfg}")
+    dev = torch.device("cuda:0")
+    inp = workload_inputs(cfg)
+    q, k, v = (inp[x].to(dev).contiguous() for x in ("q", "k", "v"))
+    m = lib.Mask(kind=w.mask, lengths=None if inp["lengths"] is None else inp["lengths"].to(dev),
+                 layout=None if inp["layout"] is None else inp["layout"].to(dev))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, lib.attn_fwd_workspace_bytes(q, k, m)), dtype=torch.uint8, device=dev)
+    med, mn, mean = time_calls(torch, lambda: lib.attn_fwd(q, k, v, mask=m, scale=inp["scale"], out=o, lse=lse,
+                                                             workspace=ws), n=calls, warm=warmup)
+    fl = 4 * w.head_dim * visible_pairs(w, inp)
+    return {"workload": w.name, "calls": calls, "fwd_ms": round(med, 5), "fwd_ms_min": round(mn, 5),
+            "fwd_ms_mean": round(mean, 5), "visible_pairs": visible_pairs(w, inp), "flops_per_call": fl,
+            "fwd_tflops": round(fl / med / 1e9, 2), "pct_peak": round(100 * fl / med / 1e9 / PEAK_BF16_TFLOPS, 2)}
+
+
 def fp8_diag(lib, torch, dev, workloads, workload_inputs):
     """Forward with fp8 (e4m3) inputs at the causal GQA workload's shape, against the same values
     in bf16; TFLOP/s counts 4*D flops per visible pair; the fp8 line is also given against the
@@ -539,11 +567,17 @@ def main():
     ap.add_argument("--all", action="store_true", help="also print forward timings of every workload to stderr")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed steps, run one device copy of this many MiB (counter calibration)")
+    ap.add_argument("--fwd-only", type=int, default=0, metavar="CONFIG",
+                    help="diagnostic: time only the forward of workload CONFIG (2-5) for --steps calls after "
+                         "--warmup calls, print one JSON line and exit (for per-workload kernel traces)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the attention path here is built and "
               "timed on a single MI355X and has no multi-GPU mode.", file=sys.stderr)
         sys.exit(2)
+    if args.fwd_only:
+        print(json.dumps(forward_only(args.fwd_only, args.steps, args.warmup)), flush=True)
+        return
     res = run_gpu(args)
     print(json.dumps(res), flush=True)
 
