@@ -426,6 +426,7 @@ def forward_all(lib, torch, dev, workloads, workload_inputs):
         log(json.dumps({"workload": w.name, "fwd_ms": round(med, 5), "fwd_ms_min": round(mn, 5),
                         "fwd_ms_mean": round(mean, 5), "fwd_tflops": round(fl / med / 1e9, 2),
                         "pct_peak": round(100 * fl / med / 1e9 / PEAK_BF16_TFLOPS, 2)}))
+    bwd_all_diag(lib, torch, dev, workloads, workload_inputs)
     split_kv_diag(lib, torch, dev)
     bwd_modes_diag(lib, torch, dev, workloads, workload_inputs)
     dense_mask_diag(lib, torch, dev)
@@ -506,6 +507,27 @@ def dense_mask_diag(lib, torch, dev):
     log(json.dumps({"workload": w.name, "visible_pairs": pairs, "fwd_ms": round(fmed, 5),
                     "fwd_tflops": round(4 * w.head_dim * pairs / fmed / 1e9, 2), "bwd_ms": round(bmed, 5),
                     "bwd_tflops": round(10 * w.head_dim * pairs / bmed / 1e9, 2)}))
+
+
+def bwd_all_diag(lib, torch, dev, workloads, workload_inputs):
+    """Backward (two-pass default, `attn_bwd` alone, O and LSE from one forward) of every bf16
+    workload with dO ~ N(0, 1) from the workload's seed: TFLOP/s counts 10*D flops per visible pair."""
+    for cfg, w in workloads.items():
+        if w.dtype != "bf16":
+            continue
+        inp = workload_inputs(cfg, with_do=True)
+        q, k, v, do = (inp[x].to(dev).contiguous() for x in ("q", "k", "v", "do"))
+        m = lib.Mask(kind=w.mask, lengths=None if inp["lengths"] is None else inp["lengths"].to(dev),
+                     layout=None if inp["layout"] is None else inp["layout"].to(dev))
+        o, lse = lib.attn_fwd(q, k, v, mask=m, scale=inp["scale"])
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = torch.empty(max(1, lib.attn_bwd_workspace_bytes(q, k, m)), dtype=torch.uint8, device=dev)
+        med, mn, _ = time_calls(torch, lambda: lib.attn_bwd(q, k, v, o, do, lse, mask=m, scale=inp["scale"], dq=dq,
+                                                             dk=dk, dv=dv, workspace=ws))
+        fl = 10 * w.head_dim * visible_pairs(w, inp)
+        log(json.dumps({"workload": w.name + "_bwd", "bwd_ms": round(med, 5), "bwd_ms_min": round(mn, 5),
+                        "bwd_tflops": round(fl / med / 1e9, 2),
+                        "pct_peak": round(100 * fl / med / 1e9 / PEAK_BF16_TFLOPS, 2)}))
 
 
 def bwd_modes_diag(lib, torch, dev, workloads, workload_inputs):
