@@ -22,7 +22,7 @@ full score matrix materialised, one (batch, head) pair at a time:
   They are written in closed form below from the chain rule through the
   softmax (the pages name the gradients but print no formula).
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
 
 * a row whose every key is masked has O = 0 and LSE = -inf (the plain formula
   gives 0/0); its gradient rows are 0;
