@@ -115,3 +115,60 @@ def test_bwd_workload_block_sparse_full_size(gpu_available):
     scale_v = dv.float().abs().sum(dim=2).clamp_min(1.0)
     assert float((dk_sum.abs() / scale_k).max()) < 2e-2
     assert float(((dv_sum - do_sum).abs() / scale_v).max()) < 2e-2
+
+
+# Query rows sampled per (b, h) at full size: the first rows, both sides of every 64-row block
+# boundary in the sample, the padding length boundary (padding workload), and the last row.
+def _sample_rows(w: Workload, inp: dict, b: int) -> list:
+    rows = {0, 1, 63, 64, 127, 128, 1000, w.seq_q // 2, w.seq_q - 1}
+    if w.mask == "padding":
+        L = int(inp["lengths"][b])
+        rows |= {L - 1, L, min(L + 1, w.seq_q - 1)}
+    return sorted(r for r in rows if 0 <= r < w.seq_q)
+
+
+@pytest.mark.parametrize("config", (3, 4))
+def test_bwd_workload_full_size_sampled(gpu_available, config):
+    """The padding (B2 H32 S4096 D128) and causal GQA (B1 Hq32 Hkv8 S8192 D128) workloads run
+    forward and backward at full size. dQ rows sampled on several heads are compared with the
+    oracle's row-local chain rule. dK and dV of every (batch, kv-head) are checked through the
+    exact identities sum_j dK_j = 0 and sum_j dV_j = sum of dO over the group's non-empty query
+    rows. The padding workload also compares one whole head against the oracle's per-head
+    backward."""
+    w = WORKLOADS[config]
+    say(f"bwd full-size workload {config} {w.name}")
+    inp = workload_inputs(config, with_do=True)
+    _, _, dq, dk, dv = _gpu_fwd_bwd(w, inp)
+    spec = oracle_mask(w, inp)
+    q64, k64, v64, do64 = (to_np64(inp[x]) for x in ("q", "k", "v", "do"))
+    heads = ((0, 0), (0, w.heads_q - 1), (w.batch - 1, w.heads_q // 2 + 1))
+    for (b, h) in heads:
+        rows = _sample_rows(w, inp, b)
+        ref = oracle.attention_dq_rows(q64, k64, v64, do64, spec, inp["scale"], b, h, rows)
+        got = to_np64(dq[b, h, rows])
+        assert np.all(np.isfinite(got))
+        e = _rel_err(got, ref)
+        say(f"  cfg{config} b{b} h{h} dq rows {rows}: rel max err {e:.3e}")
+        assert e <= TOL_BF16_BWD_REL, f"cfg{config} b{b} h{h} dq rows: {e}"
+        if w.mask == "padding":
+            L = int(inp["lengths"][b])
+            assert np.all(got[np.asarray(rows) >= L] == 0.0), "padded query rows must have zero dQ"
+    if w.mask == "padding":
+        b, h = 1, 5
+        ref = oracle.attention_bwd_head(q64, k64, v64, do64, spec, inp["scale"], b, h)
+        _check_grads((to_np64(dq[b, h]), to_np64(dk[b, h]), to_np64(dv[b, h])), ref, f"cfg{config} b{b} h{h}")
+    # identities per (b, kv head): dS rows sum to zero; P rows sum to one on non-empty rows
+    G = w.heads_q // w.heads_kv
+    do = inp["do"].float()
+    if w.mask == "padding":
+        live = torch.arange(w.seq_q)[None, :] < inp["lengths"].long()[:, None]   # [B, S] non-empty rows
+        do = do * live[:, None, :, None]
+    do_sum = do.reshape(w.batch, w.heads_kv, G, w.seq_q, w.head_dim).sum(dim=(2, 3)).to(dv.device)
+    dk_sum = dk.float().sum(dim=2)
+    dv_sum = dv.float().sum(dim=2)
+    scale_k = dk.float().abs().sum(dim=2).clamp_min(1.0)
+    scale_v = dv.float().abs().sum(dim=2).clamp_min(1.0)
+    ek = float((dk_sum.abs() / scale_k).max())
+    ev = float(((dv_sum - do_sum).abs() / scale_v).max())
+    say(f"  cfg{config} identities: sum dK {ek:.2e}, sum dV - sum dO {ev:.2e} (relative to sum |.|)")
+    assert ek < 2e-2 and ev < 2e-2
