@@ -410,8 +410,10 @@ def time_calls(torch, fn, n=20, warm=10, settle_s=0.2):
 
 def forward_all(lib, torch, dev, workloads, workload_inputs):
     """Extra diagnostics on stderr: forward-only TFLOP/s of every measured workload (median of 20
-    calls after 10 warm-up calls; min and mean alongside), then split-KV against no split on shapes
-    with few work items."""
+    calls after 10 warm-up calls; min and mean alongside) with the rate at which the call's tensors
+    move (GB/s against the 8 TB/s HBM peak, the figure for the small launch-bound workload), then
+    the backward of every bf16 workload, then split-KV against no split on shapes with few work
+    items."""
     for cfg, w in workloads.items():
         inp = workload_inputs(cfg)
         q, k, v = (inp[x].to(dev).contiguous() for x in ("q", "k", "v"))
@@ -423,9 +425,14 @@ def forward_all(lib, torch, dev, workloads, workload_inputs):
         med, mn, mean = time_calls(torch, lambda: lib.attn_fwd(q, k, v, mask=m, scale=inp["scale"], out=o, lse=lse,
                                                                  workspace=ws))
         fl = 4 * w.head_dim * visible_pairs(w, inp)
+        # bytes of the call's tensors, each moved once: Q, K, V read, O and LSE (fp32) written (for
+        # the padding workload this counts the padded rows too)
+        nbytes = (2 * q.numel() + k.numel() + v.numel()) * q.element_size() + lse.numel() * 4
         log(json.dumps({"workload": w.name, "fwd_ms": round(med, 5), "fwd_ms_min": round(mn, 5),
                         "fwd_ms_mean": round(mean, 5), "fwd_tflops": round(fl / med / 1e9, 2),
-                        "pct_peak": round(100 * fl / med / 1e9 / PEAK_BF16_TFLOPS, 2)}))
+                        "pct_peak": round(100 * fl / med / 1e9 / PEAK_BF16_TFLOPS, 2),
+                        "io_bytes": int(nbytes), "io_gbps": round(nbytes / med / 1e6, 1),
+                        "io_pct_of_hbm_peak": round(100 * nbytes / med / 1e6 / 8000.0, 3)}))
     bwd_all_diag(lib, torch, dev, workloads, workload_inputs)
     split_kv_diag(lib, torch, dev)
     bwd_modes_diag(lib, torch, dev, workloads, workload_inputs)
