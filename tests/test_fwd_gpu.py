@@ -43,6 +43,24 @@ def test_fwd_small_parity(gpu_available, case):
     compare_fwd(to_np64(o), to_np64(lse), o_ref, lse_ref, TOL_F32 if dtype == "f32" else TOL_BF16_FWD, str(case))
 
 
+# fp32 problems large enough for the tile kernel (at least 256 tiles of 64 queries and more than
+# 2^22 (query, key) pairs); the shapes above all run on the per-row fp32 kernel
+LARGE_F32 = [(d, mask) for d in (64, 128) for mask in ("none", "causal", "padding", "block", "dense")]
+
+
+@pytest.mark.parametrize("case", LARGE_F32, ids=lambda c: "-".join(map(str, c)))
+def test_fwd_f32_tile_kernel_parity(gpu_available, case):
+    d, mask = case
+    w = Workload(f"t_f32_large_{d}_{mask}", "f32", 2, 8, 4, 1024, 1024, d, mask, len_range=(300, 1024),
+                 keep_prob=0.3)
+    seed = 4100 + d
+    say(f"fwd f32 tile kernel {case} seed {seed}")
+    inp, o, lse = run_fwd(w, seed)
+    o_ref, lse_ref = oracle.attention_fwd(to_np64(inp["q"]), to_np64(inp["k"]), to_np64(inp["v"]),
+                                          oracle_mask(w, inp), inp["scale"])
+    compare_fwd(to_np64(o), to_np64(lse), o_ref, lse_ref, TOL_F32, str(case))
+
+
 @pytest.mark.parametrize("d", (64, 128))
 def test_fwd_block_per_head_layout(gpu_available, d):
     w = _small_workload("bf16", d, "block", 2, 4, 2, 300, per_head=True)
