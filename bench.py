@@ -358,9 +358,13 @@ def cpu_baseline(w, inp, pairs_total):
 
     import oracle
 
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        pools = [i for i in threadpool_info() if i.get("user_api") == "blas"] or threadpool_info()
+        cores = max((i.get("num_threads", 1) for i in pools), default=1)
+        if pools:
+            blas = ", ".join(sorted({f"{i.get('internal_api', '?')} {i.get('version', '')}".strip() for i in pools}))
     except Exception:  # noqa: BLE001
         cores = len(os.sched_getaffinity(0))
     q64, k64, v64, do64 = (inp[x].to(dtype=__import__("torch").float64).numpy() for x in ("q", "k", "v", "do"))
@@ -383,7 +387,7 @@ def cpu_baseline(w, inp, pairs_total):
     return {"value": round(flops / secs / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"fwd+bwd of {heads_done} of {total_heads} (batch, head) pairs of the same workload, "
                       f"{secs:.1f} s; value counts the same algorithmic flops per pair as the GPU line",
-            "seconds": round(secs, 2)}
+            "seconds": round(secs, 2), "blas": blas}
 
 
 def time_calls(torch, fn, n=20, warm=10, settle_s=0.2):
