@@ -7,6 +7,7 @@ fallback: if the library is missing this module raises when it is first used.
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import math
 import os
@@ -125,7 +126,10 @@ class Mask:
     dense: Optional[torch.Tensor] = None
 
     def to_c(self) -> AttnMask:
+        """The C descriptor. Call check() first: this only copies pointers and strides."""
         m = AttnMask()
+        if self.kind not in MASK_KINDS:
+            raise ValueError(f"unknown mask kind {self.kind!r}; expected one of {sorted(MASK_KINDS)}")
         m.kind = MASK_KINDS[self.kind]
         m.block_q = m.block_k = self.block
         if self.lengths is not None:
@@ -136,13 +140,39 @@ class Mask:
                 m.layout_stride_b = self.layout.stride(0)
                 m.layout_stride_h = self.layout.stride(1)
         if self.dense is not None:
-            if self.dense.element_size() != 1 or not self.dense.is_contiguous():
-                raise ValueError("dense mask must be a contiguous uint8 or bool tensor")
             m.dense = self.dense.data_ptr()
             if self.dense.dim() == 4:
                 m.dense_stride_b = self.dense.stride(0)
                 m.dense_stride_h = self.dense.stride(1)
         return m
+
+    def check(self, batch: int, heads_q: int, seq_q: int, seq_k: int, device: torch.device):
+        """Raise ValueError/TypeError unless the tensors this kind reads match the header's contract:
+        padding lengths int32 [batch]; a block layout of 1-byte elements, [nb_q, nb_k] or
+        [batch, heads_q, nb_q, nb_k] with nb = ceil(seq / block); a dense mask of 1-byte elements,
+        [seq_q, seq_k] or [batch, heads_q, seq_q, seq_k]; all contiguous and on `device`."""
+        if self.kind not in MASK_KINDS:
+            raise ValueError(f"unknown mask kind {self.kind!r}; expected one of {sorted(MASK_KINDS)}")
+
+        def need(t, name, shapes, dtypes):
+            if t is None:
+                raise ValueError(f"a {self.kind} mask needs `{name}`")
+            if t.dtype not in dtypes:
+                raise TypeError(f"mask {name} must have dtype {' or '.join(map(str, dtypes))}, got {t.dtype}")
+            if tuple(t.shape) not in shapes:
+                raise ValueError(f"mask {name} has shape {tuple(t.shape)}; expected one of {shapes}")
+            if t.device != device:
+                raise ValueError(f"mask {name} is on {t.device}, the inputs on {device}")
+            if not t.is_contiguous():
+                raise ValueError(f"mask {name} must be contiguous")
+
+        if self.kind == "padding":
+            need(self.lengths, "lengths", [(batch,)], (torch.int32,))
+        elif self.kind == "block":
+            nbq, nbk = -(-seq_q // self.block), -(-seq_k // self.block)
+            need(self.layout, "layout", [(nbq, nbk), (batch, heads_q, nbq, nbk)], (torch.uint8, torch.bool))
+        elif self.kind == "dense":
+            need(self.dense, "dense", [(seq_q, seq_k), (batch, heads_q, seq_q, seq_k)], (torch.uint8, torch.bool))
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -165,13 +195,55 @@ def _problem(q: torch.Tensor, k: torch.Tensor) -> AttnProblem:
     return p
 
 
-def _check_tensors(*ts: torch.Tensor):
-    dev = ts[0].device
-    for t in ts:
+def _expect(t: torch.Tensor, name: str, shape, dtype: torch.dtype, device: torch.device):
+    """Raise unless `t` is a contiguous tensor of this shape and dtype on `device`."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the inputs on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_inputs(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: "Mask") -> AttnProblem:
+    """Validate q, k, v and the mask against the header's layout contract; returns the problem.
+
+    q [batch, heads_q, seq_q, head_dim]; k and v [batch, heads_kv, seq_k, head_dim], one dtype,
+    contiguous, on one GPU."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.dim() != 4:
+            raise ValueError(f"{name} must be a 4-d tensor [batch, heads, seq, head_dim]")
+    prob = _problem(q, k)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError(f"q, k, v must share one dtype, got {q.dtype}, {k.dtype}, {v.dtype}")
+    if tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"v has shape {tuple(v.shape)}, k has {tuple(k.shape)}; they must match")
+    if k.shape[0] != q.shape[0] or k.shape[3] != q.shape[3]:
+        raise ValueError(f"q {tuple(q.shape)} and k {tuple(k.shape)} differ in batch or head_dim")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.device != q.device:
+            raise ValueError(f"{name} is on {t.device}, q on {q.device}")
         if not t.is_contiguous():
-            raise ValueError("libattn needs contiguous tensors")
-        if t.device != dev:
-            raise ValueError("all tensors must be on the same device")
+            raise ValueError(f"libattn needs contiguous tensors ({name} is not)")
+    mask.check(prob.batch, prob.heads_q, prob.seq_q, prob.seq_k, q.device)
+    return prob
+
+
+def _check_device(q: torch.Tensor):
+    if q.device.type != "cuda":
+        raise ValueError(f"libattn runs on the GPU; the inputs are on {q.device}")
+
+
+def _check_workspace(ws: Optional[torch.Tensor], device: torch.device):
+    if ws is not None:
+        if ws.device != device:
+            raise ValueError(f"workspace is on {ws.device}, the inputs on {device}")
+        if not ws.is_contiguous():
+            raise ValueError("workspace must be contiguous")
 
 
 def _stream_ptr(stream) -> int:
@@ -204,29 +276,44 @@ def attn_bwd_workspace_bytes(q: torch.Tensor, k: torch.Tensor, mask: Optional[Ma
     return int(lib.attn_bwd_ex_workspace_bytes(ctypes.byref(_problem(q, k)), ctypes.byref(m), int(flags)))
 
 
+def _on_stream(stream):
+    """Allocation context: tensors the binding allocates for a call belong to the stream the call's
+    kernels run on, so the caching allocator never hands them to other work while those kernels
+    may still use them."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Optional[Mask] = None,
              scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
              lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None,
              kv_splits: int = 0):
-    """Forward: returns (O, LSE). O has q's dtype; LSE is float32 [batch, heads_q, seq_q].
+    """Forward: returns (O, LSE). O has q's dtype (bf16 for fp8 inputs); LSE is float32
+    [batch, heads_q, seq_q].
 
     kv_splits: 0 lets the library choose a split of each item's key range, 1 never splits,
-    n > 1 forces n splits (attn_fwd_ex)."""
+    n > 1 forces n splits (attn_fwd_ex). Every tensor is checked against the layout of
+    include/attn.h before the call; the library itself checks sizes, alignment and overlaps."""
     lib = load_library()
-    _check_tensors(q, k, v)
     mask = mask or Mask()
-    prob = _problem(q, k)
+    prob = _check_inputs(q, k, v, mask)
+    o_dtype = torch.bfloat16 if q.dtype == torch.float8_e4m3fn else q.dtype
+    if out is not None:
+        _expect(out, "out", q.shape, o_dtype, q.device)
+    if lse is not None:
+        _expect(lse, "lse", q.shape[:3], torch.float32, q.device)
+    _check_workspace(workspace, q.device)
+    _check_device(q)
     cm = mask.to_c()
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[-1])
-    if out is None:
-        out = torch.empty(q.shape, dtype=torch.bfloat16 if q.dtype == torch.float8_e4m3fn else q.dtype,
-                          device=q.device)
-    if lse is None:
-        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     need = int(lib.attn_fwd_ex_workspace_bytes(ctypes.byref(prob), ctypes.byref(cm), int(kv_splits)))
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    with _on_stream(stream):
+        if out is None:
+            out = torch.empty(q.shape, dtype=o_dtype, device=q.device)
+        if lse is None:
+            lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = lib.attn_fwd_ex(ctypes.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(cm),
@@ -244,20 +331,29 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     """Backward: returns (dQ, dK, dV) in q's dtype.
 
     flags: 0 (two passes, deterministic) or ATTN_BWD_ATOMIC_DQ (single pass, dQ accumulated with
-    fp32 atomics; attn_bwd_ex)."""
+    fp32 atomics; attn_bwd_ex). o and do have q's shape and dtype, lse is float32
+    [batch, heads_q, seq_q]; dq, dk, dv (when given) have the shapes of q, k, v."""
     lib = load_library()
-    _check_tensors(q, k, v, o, do, lse)
     mask = mask or Mask()
-    prob = _problem(q, k)
+    prob = _check_inputs(q, k, v, mask)
+    _expect(o, "o", q.shape, q.dtype, q.device)
+    _expect(do, "do", q.shape, q.dtype, q.device)
+    _expect(lse, "lse", q.shape[:3], torch.float32, q.device)
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t is not None:
+            _expect(t, name, ref.shape, ref.dtype, q.device)
+    _check_workspace(workspace, q.device)
+    _check_device(q)
     cm = mask.to_c()
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[-1])
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
     need = int(lib.attn_bwd_ex_workspace_bytes(ctypes.byref(prob), ctypes.byref(cm), int(flags)))
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    with _on_stream(stream):
+        dq = torch.empty_like(q) if dq is None else dq
+        dk = torch.empty_like(k) if dk is None else dk
+        dv = torch.empty_like(v) if dv is None else dv
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = lib.attn_bwd_ex(ctypes.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),

@@ -5,11 +5,13 @@
 // and tiling metadata up front so that a mismatch fails at once instead of late).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
-#include <algorithm>
 #include <cstring>
 
+#include "api_internal.h"
 #include "attn.h"
 #include "kernels.h"
 #include "params.h"
@@ -154,22 +156,53 @@ int64_t fwd_items(const attn_problem* p, const attn_mask* m) {
   return (int64_t)p->batch * p->heads_q * ceil_div(p->seq_q, fwd_tile_m(p, m));
 }
 
+// Compute units and XCDs of the current device, queried once per device (plain attribute queries:
+// nothing is allocated). MI355X in its single-partition mode has 256 CUs in 8 XCDs, and the
+// dispatcher deals workgroup w to XCD w % 8; a partition mode exposes fewer of both. Without a
+// device (host-only size queries) the single-partition MI355X figures are used; if a query fails on
+// a device, the kernels get one XCD (no per-XCD grouping) and 256 CUs.
+struct DeviceInfo {
+  int32_t cus, xcds;
+};
+constexpr int kMaxDevices = 64;
+std::atomic<int32_t> g_device_info[kMaxDevices];   // cus << 8 | xcds; 0 = not yet queried
+
+DeviceInfo device_info() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return DeviceInfo{256, 8};
+  }
+  if (dev >= kMaxDevices) return DeviceInfo{256, 1};
+  int32_t v = g_device_info[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int cus = 0, xcds = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    if (hipDeviceGetAttribute(&xcds, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || xcds < 1 ||
+        xcds > kMaxXcd || cus % xcds != 0)
+      xcds = 1;
+    (void)hipGetLastError();
+    v = (std::min(cus, 1 << 22) << 8) | xcds;
+    g_device_info[dev].store(v, std::memory_order_relaxed);
+  }
+  return DeviceInfo{v >> 8, v & 0xff};
+}
+
 // Workgroups that share one item's key range (split-KV). requested: 0 = choose, 1 = never split,
 // n = n splits (at most one per 64-key tile). The automatic choice splits only when there are
-// fewer items than CUs (256), aiming at about two workgroups per CU (512 slots) and keeping at
-// least 8 key tiles per split so that the merge stays small next to the split's work. Measured:
+// fewer items than CUs, aiming at about two workgroups per CU and keeping at least 8 key tiles per
+// split so that the merge stays small next to the split's work. Measured on MI355X (256 CUs):
 // 128 items of 128 queries x 32768 keys run 1.55x faster with 4 splits; 256 items of 128 x 16384
 // run 6% slower with 2 splits than without.
 constexpr int kMaxSplits = 32;
-constexpr int64_t kCUs = 256;
-constexpr int64_t kWorkgroupSlots = 512;
 int32_t fwd_splits(const attn_problem* p, const attn_mask* m, int32_t requested) {
   if (p->dtype == ATTN_F32 || requested == 1) return 1;
   const int32_t kv_tiles = ceil_div(p->seq_k, 64);
   if (requested > 1) return std::max(1, std::min(requested, kv_tiles));
   const int64_t items = fwd_items(p, m);
-  if (items >= kCUs) return 1;
-  int64_t n = (kWorkgroupSlots + items - 1) / items;
+  const int64_t cus = device_info().cus;
+  if (items >= cus) return 1;
+  int64_t n = (2 * cus + items - 1) / items;
   n = std::min<int64_t>(n, kv_tiles / 8);
   n = std::min<int64_t>(n, kMaxSplits);
   return n >= 2 ? (int32_t)n : 1;
@@ -398,6 +431,7 @@ attn_status attn_fwd_ex(const attn_problem* problem, const void* Q, const void* 
   fp.dense_stride_b = m->dense_stride_b;
   fp.dense_stride_h = m->dense_stride_h;
   fp.kv_splits = splits;
+  fp.n_xcd = device_info().xcds;
   if (splits > 1) {
     fp.o_part = (float*)((char*)workspace + fz.o_part_off);
     fp.lse_part = (float*)((char*)workspace + fz.lse_part_off);
@@ -424,6 +458,7 @@ attn_status attn_fwd_ex(const attn_problem* problem, const void* Q, const void* 
     pp.lengths = m->lengths; pp.layout = fp.layout;
     pp.layout_stride_b = fp.layout_stride_b; pp.layout_stride_h = fp.layout_stride_h;
     pp.items = (uint32_t*)workspace;
+    pp.n_xcd = fp.n_xcd;
     st = hip_status(timed(ATTN_KERNEL_PLAN, s, [&] { return launch_plan(pp, s); }));
     if (st != ATTN_OK) return st;
     fp.items = (const uint32_t*)workspace;
@@ -457,6 +492,18 @@ attn_status attn_bwd(const attn_problem* problem, const void* Q, const void* K, 
 attn_status attn_bwd_ex(const attn_problem* problem, const void* Q, const void* K, const void* V, const void* O,
                         const void* dO, const float* LSE, const attn_mask* mask, float scale, void* dQ, void* dK,
                         void* dV, void* workspace, size_t workspace_bytes, int32_t flags, void* stream) {
+  return attn::bwd_call(problem, Q, K, V, O, dO, LSE, mask, scale, dQ, dK, dV, workspace, workspace_bytes, flags,
+                        stream, nullptr);
+}
+
+}  // extern "C"
+
+namespace attn {
+
+attn_status bwd_call(const attn_problem* problem, const void* Q, const void* K, const void* V, const void* O,
+                     const void* dO, const float* LSE, const attn_mask* mask, float scale, void* dQ, void* dK,
+                     void* dV, void* workspace, size_t workspace_bytes, int32_t flags, void* stream,
+                     WorkspaceProvider provide) {
   if (problem == nullptr || Q == nullptr || K == nullptr || V == nullptr || O == nullptr || dO == nullptr ||
       LSE == nullptr || dQ == nullptr || dK == nullptr || dV == nullptr)
     return ATTN_ERR_NULL;
@@ -475,37 +522,38 @@ attn_status attn_bwd_ex(const attn_problem* problem, const void* Q, const void* 
   for (const void* ptr : {Q, K, V, O, dO, (const void*)LSE, (const void*)dQ, (const void*)dK, (const void*)dV})
     if (!aligned16(ptr)) return ATTN_ERR_ALIGN;
   const BwdSizes bs = bwd_sizes(p, m, flags);
-  if (workspace == nullptr || workspace_bytes < bs.total) return ATTN_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
 
   const size_t es = 2;
   const size_t qbytes = (size_t)p->batch * p->heads_q * p->seq_q * p->head_dim * es;
   const size_t kvbytes = (size_t)p->batch * p->heads_kv * p->seq_k * p->head_dim * es;
   const Range ins[] = {range_of(Q, qbytes), range_of(K, kvbytes), range_of(V, kvbytes), range_of(O, qbytes),
                        range_of(dO, qbytes), range_of(LSE, (size_t)p->batch * p->heads_q * p->seq_q * 4)};
-  const Range outs[] = {range_of(dQ, qbytes), range_of(dK, kvbytes), range_of(dV, kvbytes),
-                        range_of(workspace, bs.total)};
-  for (int i = 0; i < 4; ++i) {
+  Range outs[] = {range_of(dQ, qbytes), range_of(dK, kvbytes), range_of(dV, kvbytes), Range{0, 0}};
+  Range mask_range{0, 0};
+  if (m->kind == ATTN_MASK_PADDING) mask_range = range_of(m->lengths, (size_t)p->batch * 4);
+  if (m->kind == ATTN_MASK_BLOCK) mask_range = range_of(m->block_layout, (size_t)layout_bytes(p, m));
+  if (m->kind == ATTN_MASK_DENSE) mask_range = range_of(m->dense, (size_t)dense_bytes(p, m));
+  // outputs against inputs, each other and the mask data
+  for (int i = 0; i < 3; ++i) {
     for (const Range& r : ins)
       if (overlap(outs[i], r)) return ATTN_ERR_ALIAS;
-    for (int j = i + 1; j < 4; ++j)
+    for (int j = i + 1; j < 3; ++j)
       if (overlap(outs[i], outs[j])) return ATTN_ERR_ALIAS;
+    if (overlap(mask_range, outs[i])) return ATTN_ERR_ALIAS;
   }
-  if (m->kind == ATTN_MASK_PADDING) {
-    const Range rlen = range_of(m->lengths, (size_t)p->batch * 4);
-    for (const Range& r : outs)
-      if (overlap(rlen, r)) return ATTN_ERR_ALIAS;
+  // the workspace: the caller's, or (for the no-allocation entry point) one the provider names
+  if (provide != nullptr) {
+    st = provide(bs.total, &workspace, &workspace_bytes);
+    if (st != ATTN_OK) return st;
   }
-  if (m->kind == ATTN_MASK_BLOCK) {
-    const Range rlay = range_of(m->block_layout, (size_t)layout_bytes(p, m));
-    for (const Range& r : outs)
-      if (overlap(rlay, r)) return ATTN_ERR_ALIAS;
-  }
-  if (m->kind == ATTN_MASK_DENSE) {
-    const Range rden = range_of(m->dense, (size_t)dense_bytes(p, m));
-    for (const Range& r : outs)
-      if (overlap(rden, r)) return ATTN_ERR_ALIAS;
-  }
+  if (workspace == nullptr || workspace_bytes < bs.total) return ATTN_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
+  outs[3] = range_of(workspace, bs.total);
+  for (int i = 0; i < 3; ++i)
+    if (overlap(outs[3], outs[i])) return ATTN_ERR_ALIAS;
+  for (const Range& r : ins)
+    if (overlap(outs[3], r)) return ATTN_ERR_ALIAS;
+  if (overlap(mask_range, outs[3])) return ATTN_ERR_ALIAS;
 
   hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
@@ -543,6 +591,7 @@ attn_status attn_bwd_ex(const attn_problem* problem, const void* Q, const void* 
   pp.group = bp.group; pp.seq_q = p->seq_q; pp.seq_k = p->seq_k;
   pp.nb_q = bp.nb_q; pp.nb_k = bp.nb_k; pp.lengths = m->lengths; pp.layout = bp.layout;
   pp.layout_stride_b = bp.layout_stride_b; pp.layout_stride_h = bp.layout_stride_h;
+  pp.n_xcd = device_info().xcds;
   // dK/dV items (b, kv head, key tile) and dQ items (b, query head, query tile), one launch
   PlanParams pk = pp, pq = pp;
   pk.mode = PLAN_BWD_KV; pk.heads = p->heads_kv; pk.n_tiles = bs.n_kt; pk.tile = bs.bk;
@@ -573,4 +622,4 @@ attn_status attn_bwd_ex(const attn_problem* problem, const void* Q, const void* 
                           [&] { return launch_bwd_dkdv(bp, p->head_dim, m->kind, (int)bs.kv_items, s); }));
 }
 
-}  // extern "C"
+}  // namespace attn

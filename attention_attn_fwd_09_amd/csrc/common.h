@@ -128,20 +128,20 @@ __device__ __forceinline__ Item decode_item(uint32_t it, int heads_q, int n_qtil
 }
 
 // Closed-form longest-first order for masks whose per-tile cost is known without data (NONE, CAUSAL).
-// Workgroup i runs on XCD i % 8; when the (batch, kv-head) units divide evenly over the 8 XCDs, all
-// items of one unit go to one XCD so that its K/V stay in that XCD's L2.
+// The dispatcher deals workgroup i to XCD i % n_xcd; when the (batch, kv-head) units divide evenly
+// over the XCDs, all items of one unit go to one XCD so that its K/V stay in that XCD's L2.
 __device__ __forceinline__ Item closed_form_item(int i, int batch, int heads_q, int heads_kv, int n_qtiles,
-                                                 bool descending) {
+                                                 bool descending, int n_xcd) {
   const int group = heads_q / heads_kv;
   const int units = batch * heads_kv;
   Item r;
   int rank;
-  if ((units & 7) == 0) {
-    const int xcd = i & 7, slot = i >> 3;
-    const int per_rank = (units >> 3) * group;
+  if (n_xcd > 1 && units % n_xcd == 0) {
+    const int xcd = i % n_xcd, slot = i / n_xcd;
+    const int per_rank = (units / n_xcd) * group;
     rank = slot / per_rank;
     const int rem = slot - rank * per_rank;
-    const int unit = xcd + 8 * (rem / group);
+    const int unit = xcd + n_xcd * (rem / group);
     r.b = unit / heads_kv;
     r.h = (unit - r.b * heads_kv) * group + rem % group;
   } else {
@@ -153,6 +153,23 @@ __device__ __forceinline__ Item closed_form_item(int i, int batch, int heads_q, 
   }
   r.t = descending ? (n_qtiles - 1 - rank) : rank;
   return r;
+}
+
+// Split-KV launches kv_splits workgroups per item. Workgroup w runs on XCD w % n_xcd; the item list
+// (closed form or planner) places item i on XCD i % n_xcd. So that all splits of an item share its
+// XCD's L2, the workgroups of each XCD take that XCD's items in list order, kv_splits consecutive
+// workgroups per item. This is a bijection between workgroups and (item, split) pairs whenever
+// n_items divides by n_xcd; otherwise workgroups take items in plain order.
+__device__ __forceinline__ void split_item(uint32_t w, int n_items, int kv_splits, int n_xcd, int& item_idx,
+                                           int& split) {
+  if (kv_splits > 1 && n_xcd > 1 && n_items % n_xcd == 0) {
+    const uint32_t xcd = w % (uint32_t)n_xcd, slot = w / (uint32_t)n_xcd;
+    item_idx = (int)((slot / (uint32_t)kv_splits) * (uint32_t)n_xcd + xcd);
+    split = (int)(slot % (uint32_t)kv_splits);
+  } else {
+    item_idx = (int)(w / (uint32_t)kv_splits);
+    split = (int)(w % (uint32_t)kv_splits);
+  }
 }
 
 __device__ __forceinline__ int clamp_len(int32_t len, int seq) { return len < 0 ? 0 : (len > seq ? seq : len); }

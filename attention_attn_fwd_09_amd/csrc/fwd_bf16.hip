@@ -69,11 +69,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
   const int i16 = lane & 15, dsub = ((lane >> 4) & 1) * 16;
 
   // ---- which tile of which (batch, head), and which part of its key range (split-KV) ----
-  const int split = (int)(blockIdx.x % (uint32_t)p.kv_splits);
-  const int item_idx = (int)(blockIdx.x / (uint32_t)p.kv_splits);
+  int item_idx, split;
+  split_item(blockIdx.x, p.n_items, p.kv_splits, p.n_xcd, item_idx, split);
   Item it;
   if constexpr (MASK == MASK_NONE || MASK == MASK_CAUSAL) {
-    it = closed_form_item(item_idx, p.batch, p.heads_q, p.heads_kv, p.n_qtiles, MASK == MASK_CAUSAL);
+    it = closed_form_item(item_idx, p.batch, p.heads_q, p.heads_kv, p.n_qtiles, MASK == MASK_CAUSAL, p.n_xcd);
   } else {
     it = decode_item(p.items[item_idx], p.heads_q, p.n_qtiles);
   }

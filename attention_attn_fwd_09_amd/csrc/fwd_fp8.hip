@@ -92,11 +92,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
   const int c = lane & 31, hh = lane >> 5;
   const int i16 = lane & 15, g16 = lane >> 4;
 
-  const int split = (int)(blockIdx.x % (uint32_t)p.kv_splits);
-  const int item_idx = (int)(blockIdx.x / (uint32_t)p.kv_splits);
+  int item_idx, split;
+  split_item(blockIdx.x, p.n_items, p.kv_splits, p.n_xcd, item_idx, split);
   Item it;
   if constexpr (MASK == MASK_NONE || MASK == MASK_CAUSAL) {
-    it = closed_form_item(item_idx, p.batch, p.heads_q, p.heads_kv, p.n_qtiles, MASK == MASK_CAUSAL);
+    it = closed_form_item(item_idx, p.batch, p.heads_q, p.heads_kv, p.n_qtiles, MASK == MASK_CAUSAL, p.n_xcd);
   } else {
     it = decode_item(p.items[item_idx], p.heads_q, p.n_qtiles);
   }

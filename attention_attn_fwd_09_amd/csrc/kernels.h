@@ -25,8 +25,11 @@ struct PlanParams {
   const int32_t* lengths;
   const uint8_t* layout;
   int64_t layout_stride_b, layout_stride_h;
+  int32_t n_xcd;         // XCDs workgroups are dealt to round robin (at most kMaxXcd; 1 = no grouping)
   uint32_t* items;       // output: item ids, longest first
 };
+
+constexpr int kMaxXcd = 8;   // XCDs the planner can group items for
 
 // Dense element mask -> row bits, column bits (optional) and a 64x64 block layout.
 struct DensePackParams {

@@ -41,6 +41,7 @@ struct FwdParams {
   const uint8_t* dense_bytes;   // MASK_DENSE (fp32 kernel): the caller's byte mask
   int64_t dense_stride_b, dense_stride_h;
   int32_t kv_splits;            // workgroups sharing one item's key range (1 = no split)
+  int32_t n_xcd;                // XCDs the dispatcher deals workgroups to, round robin (1 = no grouping)
   float* o_part;                // kv_splits > 1: per-split O (normalised over the split), fp32
                                 //   [kv_splits][batch * heads_q * seq_q][head_dim]
   float* lse_part;              // kv_splits > 1: per-split log2-sum-exp, fp32 [kv_splits][rows]

@@ -20,9 +20,8 @@ namespace attn {
 
 namespace {
 
-constexpr int NXCD = 8;        // workgroup i is dispatched to XCD i % 8
 constexpr int NCOST = 1024;   // cost buckets per XCD; larger costs share the top bucket
-constexpr int NBUCKET = NXCD * NCOST;
+constexpr int NBUCKET = kMaxXcd * NCOST;
 constexpr int THREADS = 1024;
 
 constexpr int MAX_CACHED = 16384;  // items whose cost is kept in LDS between the passes
@@ -185,13 +184,15 @@ __device__ __forceinline__ void plan_items(const PlanParams& p) {
     }
     __syncthreads();
   }
-  // Items of one (batch, kv-head) unit share K and V (forward, dQ) or Q and dO (dK/dV); when the
-  // units divide evenly over the XCDs, unit u goes to XCD u % 8 so that its data stay in one L2.
-  // Within an XCD items are ordered longest first. Bucket xcd * NCOST + (NCOST - 1 - cost).
+  // Items of one (batch, kv-head) unit share K and V (forward, dQ) or Q and dO (dK/dV). The
+  // dispatcher deals workgroup w to XCD w % n_xcd; when the units divide evenly over the XCDs,
+  // unit u goes to XCD u % n_xcd (list positions rank * n_xcd + xcd) so that its data stay in one
+  // L2. Within an XCD items are ordered longest first. Bucket xcd * NCOST + (NCOST - 1 - cost).
   const int items_per_unit = p.mode == PLAN_BWD_KV ? p.n_tiles : p.group * p.n_tiles;
   const int n_units = p.n_items / items_per_unit;
-  const bool spread = (n_units % NXCD) == 0;
-  auto xcd_of = [&](int i) { return spread ? (i / items_per_unit) % NXCD : 0; };
+  const int n_xcd = p.n_xcd;
+  const bool spread = n_xcd > 1 && n_xcd <= kMaxXcd && (n_units % n_xcd) == 0;
+  auto xcd_of = [&](int i) { return spread ? (i / items_per_unit) % n_xcd : 0; };
   for (int i = threadIdx.x; i < p.n_items; i += THREADS) {
     const int cost = min(item_cost(p, (uint32_t)i, sh, tab_units, tab_len), NCOST - 1);
     if (cache) cached[i] = (uint16_t)cost;
@@ -213,12 +214,12 @@ __device__ __forceinline__ void plan_items(const PlanParams& p) {
     off += local[k];
   }
   __syncthreads();
-  const int per_xcd = spread ? p.n_items / NXCD : p.n_items;
+  const int per_xcd = spread ? p.n_items / n_xcd : p.n_items;
   for (int i = threadIdx.x; i < p.n_items; i += THREADS) {
     const int cost = cache ? (int)cached[i] : min(item_cost(p, (uint32_t)i, sh, tab_units, tab_len), NCOST - 1);
     const int x = xcd_of(i);
     const int rank = atomicAdd(&bucket[x * NCOST + NCOST - 1 - cost], 1) - x * per_xcd;
-    p.items[spread ? rank * NXCD + x : rank] = (uint32_t)i;
+    p.items[spread ? rank * n_xcd + x : rank] = (uint32_t)i;
   }
 }
 

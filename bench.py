@@ -10,6 +10,10 @@ Prints one JSON line. `value` is algorithmic TFLOP/s: 4*D flops per visible (que
 the forward plus 10*D for the backward (five products); masked and skipped work is not counted.
 `roofline` describes the dominant kernel, timed live with HIP events on the library's stream;
 `cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same workload.
+`workloads` holds every measured workload on its own, measured before the headline step: the fp32
+workload (batch 1, 2 heads, seq 64, head_dim 64) in microseconds and GB/s against the 8 TB/s HBM
+peak; the forward of the four bf16 workloads and the backward of the block-sparse one in TFLOP/s
+and % of the bf16 MFMA peak, each with a live-timed roofline entry for its kernels.
 Secondary figures, measured after the timed region: `cold_cache` (the same step with 512 MiB
 written before each one, so that the inputs come from HBM) and `gfx_clock` (the graphics clock
 amdsmi reports while the step runs, giving `pct_of_clock_adjusted_bf16_peak`).
@@ -128,6 +132,122 @@ def hbm_traffic(kernel: str, workload: str):
     return None
 
 
+KERNEL_CLASS = {v: k for k, v in KERNEL_NAMES.items()}
+
+
+def set_hook(clib, cls, st, sp, cap, cnt):
+    rc = clib.attn_set_timing_events(cls, st, sp, cap, ctypes.byref(cnt) if cnt is not None else None)
+    if rc != 0:
+        raise RuntimeError(f"attn_set_timing_events({cls}) failed: {rc}")
+
+
+def timed_calls(torch, fn, clib, hip, classes, n=20, warm=10, settle_s=0.2):
+    """Median ms of n calls of fn (one torch event pair per call on the current stream, which is the
+    library's stream), after `warm` calls and settle_s seconds of untimed calls so that the clocks
+    have left their idle state; and, for each kernel class in `classes`, the median over the same
+    calls of that class's kernel time per call (HIP events the library records around each launch of
+    the class on its stream). Returns (call_ms, {class: (kernel_ms, launches_per_call)})."""
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    t_end = time.perf_counter() + settle_s
+    while time.perf_counter() < t_end:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+    cap = 4 * n
+    hooks = {}
+    for cls in classes:
+        st, sp, cnt = hip.create(cap), hip.create(cap), ctypes.c_int32(0)
+        set_hook(clib, cls, st, sp, cap, cnt)
+        hooks[cls] = (st, sp, cnt)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    calls = sorted(a.elapsed_time(b) for a, b in ev)
+    kernels = {}
+    for cls, (st, sp, cnt) in hooks.items():
+        set_hook(clib, cls, None, None, 0, None)
+        k = cnt.value // n
+        per_call = sorted(sum(hip.elapsed_ms(st[i * k + j], sp[i * k + j]) for j in range(k)) for i in range(n)) \
+            if k > 0 else [0.0]
+        kernels[cls] = (per_call[len(per_call) // 2], k)
+        hip.destroy(st)
+        hip.destroy(sp)
+    return calls[len(calls) // 2], kernels
+
+
+def kernel_roofline(name, ms, flops):
+    """Roofline entry of one kernel: executed algorithmic flops per launch over its median time."""
+    achieved = flops / (ms * 1e-3) / 1e12 if ms > 0 else 0.0
+    return {"kernel": name, "ms": round(ms, 5), "bound": "mfma", "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+
+
+def measure_workloads(lib, torch, dev, clib, hip):
+    """Every measured workload, each timed on its own (median of 20 calls after warm-up):
+    c1 (fp32, launch-bound) in microseconds and GB/s of the call's tensors against the 8 TB/s HBM
+    peak; c2-c5 forward, and the c5 backward, in algorithmic TFLOP/s (4*D flops per visible pair
+    forward, 10*D backward) and % of the bf16 MFMA peak, each with its kernels' live-timed
+    roofline entries (forward kernel: 4*D flops per visible pair; dK/dV pass 8*D; dQ pass 6*D)."""
+    from attention_attn_fwd_09_amd.inputs import WORKLOADS, workload_inputs
+
+    out = {}
+    for cfg, w in WORKLOADS.items():
+        inp = workload_inputs(cfg, with_do=w.backward)
+        q, k, v = (inp[x].to(dev).contiguous() for x in ("q", "k", "v"))
+        m = lib.Mask(kind=w.mask, lengths=None if inp["lengths"] is None else inp["lengths"].to(dev),
+                     layout=None if inp["layout"] is None else inp["layout"].to(dev))
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        ws = torch.empty(max(1, lib.attn_fwd_workspace_bytes(q, k, m)), dtype=torch.uint8, device=dev)
+        pairs = visible_pairs(w, inp)
+        d = w.head_dim
+
+        def fwd():
+            lib.attn_fwd(q, k, v, mask=m, scale=inp["scale"], out=o, lse=lse, workspace=ws)
+
+        ms, kern = timed_calls(torch, fwd, clib, hip, (KERNEL_CLASS["fwd"], KERNEL_CLASS["plan"]))
+        fl = 4 * d * pairs
+        line = {"workload": w.name, "fwd_ms": round(ms, 5), "fwd_tflops": round(fl / ms / 1e9, 2),
+                "fwd_pct_of_bf16_peak": round(100 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2), "visible_pairs": pairs}
+        if w.dtype == "f32":
+            nbytes = (2 * q.numel() + k.numel() + v.numel()) * q.element_size() + lse.numel() * 4
+            line.update({"fwd_us": round(ms * 1e3, 2), "io_bytes": int(nbytes),
+                         "io_gb_s": round(nbytes / ms / 1e6, 2),
+                         "io_pct_of_hbm_peak": round(100 * nbytes / ms / 1e6 / PEAK_HBM_GBS, 4),
+                         "bound": "launch latency (2 work items)"})
+            fk = kern[KERNEL_CLASS["fwd"]][0]
+            line["kernel"] = {"kernel": "fwd_f32", "us": round(fk * 1e3, 2),
+                              "gb_s": round(nbytes / fk / 1e6, 2) if fk > 0 else None}
+        else:
+            line["roofline"] = kernel_roofline("fwd", kern[KERNEL_CLASS["fwd"]][0], fl)
+            line["plan_ms"] = round(kern[KERNEL_CLASS["plan"]][0], 5)
+        if w.backward:
+            do = inp["do"].to(dev).contiguous()
+            dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+            wsb = torch.empty(max(1, lib.attn_bwd_workspace_bytes(q, k, m)), dtype=torch.uint8, device=dev)
+            fwd()
+
+            def bwd():
+                lib.attn_bwd(q, k, v, o, do, lse, mask=m, scale=inp["scale"], dq=dq, dk=dk, dv=dv, workspace=wsb)
+
+            cls = (KERNEL_CLASS["bwd_dkdv"], KERNEL_CLASS["bwd_dq"], KERNEL_CLASS["plan"])
+            bms, bk = timed_calls(torch, bwd, clib, hip, cls)
+            bfl = 10 * d * pairs
+            line.update({"bwd_ms": round(bms, 5), "bwd_tflops": round(bfl / bms / 1e9, 2),
+                         "bwd_pct_of_bf16_peak": round(100 * bfl / bms / 1e9 / PEAK_BF16_TFLOPS, 2),
+                         "bwd_roofline": [kernel_roofline("bwd_dkdv", bk[cls[0]][0], 8 * d * pairs),
+                                          kernel_roofline("bwd_dq", bk[cls[1]][0], 6 * d * pairs)],
+                         "bwd_plan_ms": round(bk[cls[2]][0], 5)})
+        log(json.dumps(line))
+        out[f"c{cfg}"] = line
+    return out
+
+
 def run_gpu(args):
     import torch
 
@@ -169,11 +289,15 @@ def run_gpu(args):
                                             ctypes.POINTER(ctypes.c_int32)]
     clib.attn_set_timing_events.restype = ctypes.c_int
 
+    # every workload on its own, before the headline step (this also takes the clocks out of their
+    # idle state, so that the short default warm-up measures the steady state)
+    workloads = measure_workloads(lib, torch, dev, clib, hip)
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # which kernel dominates: bracket every class for a few untimed steps
+    # which kernel dominates the step: bracket every class for a few untimed steps
     probe_steps = 3
     cap = 4 * probe_steps
     probes = {}
@@ -193,8 +317,8 @@ def run_gpu(args):
         hip.destroy(st)
         hip.destroy(sp)
     dominant = max(per_class, key=lambda c: per_class[c][0])
-    log("per-step kernel time (ms): " + ", ".join(f"{KERNEL_NAMES[c]}={per_class[c][0]:.4f}x{per_class[c][1]}"
-                                                  for c in per_class))
+    log("untimed probe steps, kernel ms per step: " +
+        ", ".join(f"{KERNEL_NAMES[c]}={per_class[c][0]:.4f}x{per_class[c][1]}" for c in per_class))
 
     # timed region: the dominant kernel is bracketed on the library's stream
     st, sp = hip.create(args.steps), hip.create(args.steps)
@@ -256,7 +380,7 @@ def run_gpu(args):
         "pct_of_bf16_mfma_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "wall_s_timed": round(wall, 4),
         "roofline": roofline,
-        "kernels_ms_per_step": {KERNEL_NAMES[c]: round(per_class[c][0], 5) for c in per_class},
+        "workloads": workloads,
     }
     # secondary figures, measured after the timed region: the same step with cold caches, and the
     # graphics clock the step runs at (for the clock-adjusted peak)

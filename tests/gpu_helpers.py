@@ -69,3 +69,62 @@ def compare_fwd(o_gpu: np.ndarray, lse_gpu: np.ndarray, o_ref: np.ndarray, lse_r
     say(f"  {label}: max|dO|={err_o:.3e} max|dLSE|={err_l:.3e} (tol {tol})")
     assert err_o <= tol, f"{label}: max |O - O_ref| = {err_o} > {tol}"
     assert err_l <= tol, f"{label}: max |LSE - LSE_ref| = {err_l} > {tol}"
+
+
+def oracle_map(fn, items, workers=None):
+    """fn over items on a thread pool (numpy releases the GIL in its matmuls and element-wise
+    kernels, so per-head oracle evaluations run in parallel), BLAS limited to one thread per worker."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+
+    workers = workers or max(1, min(8, len(os.sched_getaffinity(0))))
+    with threadpool_limits(limits=1 if workers > 1 else None, user_api="blas"):
+        with ThreadPoolExecutor(workers) as ex:
+            return list(ex.map(fn, items))
+
+
+def nan_filled(shape, dtype, dev="cuda") -> torch.Tensor:
+    """An output buffer filled with NaN, so that any element a kernel fails to write shows up."""
+    return torch.full(tuple(shape), float("nan"), dtype=dtype, device=dev)
+
+
+def fwd_into_nan(w: Workload, inp: dict, kv_splits: int = 0):
+    """GPU forward of `inp` into NaN-filled O and LSE; returns (o, lse) on the device."""
+    d = device_inputs(inp)
+    q = d["q"]
+    o = nan_filled(q.shape, torch.bfloat16 if q.dtype == torch.float8_e4m3fn else q.dtype)
+    lse = nan_filled(q.shape[:3], torch.float32)
+    libattn.attn_fwd(q, d["k"], d["v"], mask=lib_mask(w, d), scale=inp["scale"], out=o, lse=lse,
+                     kv_splits=kv_splits)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def bwd_into_nan(w: Workload, inp: dict, o: torch.Tensor, lse: torch.Tensor, flags: int = 0):
+    """GPU backward (given the GPU forward's O and LSE) into NaN-filled dQ, dK, dV."""
+    d = device_inputs(inp)
+    dq = nan_filled(d["q"].shape, d["q"].dtype)
+    dk = nan_filled(d["k"].shape, d["k"].dtype)
+    dv = nan_filled(d["v"].shape, d["v"].dtype)
+    libattn.attn_bwd(d["q"], d["k"], d["v"], o, d["do"], lse, mask=lib_mask(w, d), scale=inp["scale"], dq=dq, dk=dk,
+                     dv=dv, flags=flags)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    """max|got - ref| / max|ref| (the absolute error when ref is all zero)."""
+    num = float(np.max(np.abs(got - ref))) if got.size else 0.0
+    den = float(np.max(np.abs(ref))) if ref.size else 0.0
+    return num / den if den > 0.0 else num
+
+
+def check_grads(grads_gpu, grads_ref, label: str):
+    """Each of dQ, dK, dV finite and within TOL_BF16_BWD_REL of the oracle (max-norm relative)."""
+    for name, got, ref in zip(("dq", "dk", "dv"), grads_gpu, grads_ref):
+        assert np.all(np.isfinite(got)), f"{label} {name}: non-finite values (an unwritten element stays NaN)"
+        e = rel_err(got, ref)
+        say(f"  {label} {name}: rel max err {e:.3e}")
+        assert e <= TOL_BF16_BWD_REL, f"{label} {name}: rel max err {e} > {TOL_BF16_BWD_REL}"

@@ -76,9 +76,13 @@ def test_row_subset_matches_full_oracle():
     r = np.random.default_rng(3)
     q, k, v = r.standard_normal((2, 4, 70, 8)), r.standard_normal((2, 2, 70, 8)), r.standard_normal((2, 2, 70, 8))
     lay = (r.random((2, 2)) < 0.5).astype(np.uint8)
+    dense = (r.random((70, 70)) < 0.4).astype(np.uint8)
+    dense[5] = 0                                   # a row that sees nothing
+    dense4 = (r.random((2, 4, 70, 70)) < 0.4).astype(np.uint8)
     specs = [oracle.MaskSpec("none"), oracle.MaskSpec("causal"),
              oracle.MaskSpec("padding", lengths=np.array([30, 70], np.int32)),
-             oracle.MaskSpec("block", layout=lay)]
+             oracle.MaskSpec("block", layout=lay), oracle.MaskSpec("dense", dense=dense),
+             oracle.MaskSpec("dense", dense=dense4)]
     rows = np.array([0, 5, 31, 63, 64, 69])
     for spec in specs:
         o, lse = oracle.attention_fwd(q, k, v, spec, 0.3)
@@ -99,8 +103,13 @@ def test_bwd_head_matches_full_oracle():
     q, k, v = r.standard_normal((2, 4, 40, 8)), r.standard_normal((2, 2, 40, 8)), r.standard_normal((2, 2, 40, 8))
     do = r.standard_normal(q.shape)
     lay4 = (r.random((2, 4, 1, 1)) < 2).astype(np.uint8)
-    for spec in (oracle.MaskSpec("causal"), oracle.MaskSpec("padding", lengths=np.array([13, 40], np.int32)),
-                 oracle.MaskSpec("block", layout=lay4)):
+    dense = (r.random((40, 40)) < 0.4).astype(np.uint8)
+    dense4 = (r.random((2, 4, 40, 40)) < 0.4).astype(np.uint8)
+    dense4[1, 2, 7] = 0                            # a row that sees nothing
+    for spec in (oracle.MaskSpec("none"), oracle.MaskSpec("causal"),
+                 oracle.MaskSpec("padding", lengths=np.array([13, 40], np.int32)),
+                 oracle.MaskSpec("block", layout=lay4), oracle.MaskSpec("dense", dense=dense),
+                 oracle.MaskSpec("dense", dense=dense4)):
         dq, dk, dv = oracle.attention_bwd(q, k, v, do, spec, 0.5)
         dk_sum, dv_sum = np.zeros_like(dk), np.zeros_like(dv)
         for b in range(2):

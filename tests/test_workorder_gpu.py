@@ -1,0 +1,82 @@
+"""Element-wise GPU parity on shapes whose (batch, key/value head) units divide over the 8 XCDs.
+
+When batch * heads_kv is a multiple of 8, the kernels group the work items of each unit on one
+XCD: the closed-form order of the no-mask and causal forward (bf16 and fp8), and the planner's
+per-XCD order for the padding and block masks (forward list, the backward's dK/dV and dQ lists).
+These shapes reach exactly those branches at sizes the oracle checks element by element, with
+several tiles and ragged tails. Outputs are written into NaN-filled buffers, so an item that was
+skipped, or written twice in place of another, fails the comparison.
+"""
+
+import pytest
+
+import oracle
+from attention_attn_fwd_09_amd import binding as libattn
+from attention_attn_fwd_09_amd.inputs import Workload, make_inputs
+from tests.gpu_helpers import (TOL_BF16_FWD, bwd_into_nan, check_grads, compare_fwd, fwd_into_nan, oracle_mask, say,
+                               to_np64)
+from tests.test_fp8_gpu import _check as check_fp8
+
+pytestmark = pytest.mark.gpu
+
+# (batch, heads_q, heads_kv, seq): batch * heads_kv is 8 or 16
+SHAPES = ((2, 8, 4, 200), (4, 8, 4, 130), (1, 16, 8, 333), (8, 1, 1, 100), (16, 2, 1, 70))
+
+
+def _w(dtype, d, mask, b, hq, hkv, s, backward=False):
+    return Workload(f"xcd_{dtype}_{d}_{mask}_{b}_{hq}_{hkv}_{s}", dtype, b, hq, hkv, s, s, d, mask,
+                    backward=backward, len_range=(max(1, s // 4), s), keep_prob=0.3)
+
+
+FWD = [(dt, d, mask, *shape) for dt in ("bf16", "fp8") for d in (64, 128)
+       for mask in ("none", "causal", "padding", "block") for shape in SHAPES]
+
+
+@pytest.mark.parametrize("case", FWD, ids=lambda c: "-".join(map(str, c)))
+def test_fwd_xcd_grouped_order(gpu_available, case):
+    dt, d, mask, b, hq, hkv, s = case
+    w = _w(dt, d, mask, b, hq, hkv, s)
+    seed = 500 + s + d
+    say(f"fwd xcd-grouped {case} seed {seed}")
+    inp = make_inputs(w, seed)
+    o, lse = fwd_into_nan(w, inp)
+    if dt == "fp8":
+        check_fp8(w, inp, o, lse, str(case))
+        return
+    o_ref, lse_ref = oracle.attention_fwd(to_np64(inp["q"]), to_np64(inp["k"]), to_np64(inp["v"]),
+                                          oracle_mask(w, inp), inp["scale"])
+    compare_fwd(to_np64(o), to_np64(lse), o_ref, lse_ref, TOL_BF16_FWD, str(case))
+
+
+SPLIT = [(d, mask, splits) for d in (64, 128) for mask in ("none", "causal", "padding", "block") for splits in (2, 3)]
+
+
+@pytest.mark.parametrize("case", SPLIT, ids=lambda c: "-".join(map(str, c)))
+def test_fwd_xcd_grouped_split_kv(gpu_available, case):
+    """Split-KV on an XCD-grouped shape: the splits of one item take consecutive slots of its XCD."""
+    d, mask, splits = case
+    w = _w("bf16", d, mask, 2, 8, 4, 700)
+    inp = make_inputs(w, 900 + d + splits)
+    say(f"fwd xcd-grouped split-kv {case}")
+    o, lse = fwd_into_nan(w, inp, kv_splits=splits)
+    o_ref, lse_ref = oracle.attention_fwd(to_np64(inp["q"]), to_np64(inp["k"]), to_np64(inp["v"]),
+                                          oracle_mask(w, inp), inp["scale"])
+    compare_fwd(to_np64(o), to_np64(lse), o_ref, lse_ref, TOL_BF16_FWD, str(case))
+
+
+BWD = [(d, mask, flags, *shape) for d in (64, 128) for mask in ("none", "causal", "padding", "block")
+       for flags in (0, libattn.ATTN_BWD_ATOMIC_DQ) for shape in SHAPES[:3]]
+
+
+@pytest.mark.parametrize("case", BWD, ids=lambda c: "-".join(map(str, c)))
+def test_bwd_xcd_grouped_order(gpu_available, case):
+    d, mask, flags, b, hq, hkv, s = case
+    w = _w("bf16", d, mask, b, hq, hkv, s, backward=True)
+    seed = 700 + s + d
+    say(f"bwd xcd-grouped {case} seed {seed}")
+    inp = make_inputs(w, seed)
+    o, lse = fwd_into_nan(w, inp)
+    grads = bwd_into_nan(w, inp, o, lse, flags=flags)
+    ref = oracle.attention_bwd(to_np64(inp["q"]), to_np64(inp["k"]), to_np64(inp["v"]), to_np64(inp["do"]),
+                               oracle_mask(w, inp), inp["scale"])
+    check_grads(tuple(to_np64(g) for g in grads), ref, str(case))
