@@ -29,6 +29,7 @@ ATTN_ERR_WORKSPACE = 6
 ATTN_ERR_ALIAS = 7
 ATTN_ERR_UNSUPPORTED = 8
 ATTN_ERR_HIP = 9
+ATTN_ERR_TOO_LARGE = 10
 
 ATTN_F32 = 0
 ATTN_BF16 = 1
@@ -97,6 +98,10 @@ def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
     lib.attn_bwd_ex.restype = ctypes.c_int
     lib.attn_bwd_ex_workspace_bytes.argtypes = [pp, pm, ctypes.c_int32]
     lib.attn_bwd_ex_workspace_bytes.restype = sz
+    lib.attn_bwd_noalloc.argtypes = [pp, vp, vp, vp, vp, vp, vp, pm, ctypes.c_float, vp, vp, vp, vp]
+    lib.attn_bwd_noalloc.restype = ctypes.c_int
+    lib.attn_bwd_noalloc_scratch_bytes.argtypes = []
+    lib.attn_bwd_noalloc_scratch_bytes.restype = sz
     lib.attn_status_string.argtypes = [ctypes.c_int]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -359,5 +364,34 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     st = lib.attn_bwd_ex(ctypes.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                          do.data_ptr(), lse.data_ptr(), ctypes.byref(cm), float(scale), dq.data_ptr(), dk.data_ptr(),
                          dv.data_ptr(), ws_ptr, ws_bytes, int(flags), _stream_ptr(stream))
+    _raise(st)
+    return dq, dk, dv
+
+
+def attn_bwd_noalloc_scratch_bytes() -> int:
+    """Bytes of the fixed device array attn_bwd_noalloc uses as its workspace."""
+    return int(load_library().attn_bwd_noalloc_scratch_bytes())
+
+
+def attn_bwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, do: torch.Tensor,
+                     lse: torch.Tensor, dq: torch.Tensor, dk: torch.Tensor, dv: torch.Tensor,
+                     mask: Optional[Mask] = None, scale: Optional[float] = None, stream=None):
+    """attn_bwd without a workspace (the library's fixed scratch array serves instead); dq, dk, dv
+    are caller-provided outputs, so this call allocates nothing. Returns (dq, dk, dv)."""
+    lib = load_library()
+    mask = mask or Mask()
+    prob = _check_inputs(q, k, v, mask)
+    _expect(o, "o", q.shape, q.dtype, q.device)
+    _expect(do, "do", q.shape, q.dtype, q.device)
+    _expect(lse, "lse", q.shape[:3], torch.float32, q.device)
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _expect(t, name, ref.shape, ref.dtype, q.device)
+    _check_device(q)
+    cm = mask.to_c()
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    st = lib.attn_bwd_noalloc(ctypes.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                              do.data_ptr(), lse.data_ptr(), ctypes.byref(cm), float(scale), dq.data_ptr(),
+                              dk.data_ptr(), dv.data_ptr(), _stream_ptr(stream))
     _raise(st)
     return dq, dk, dv

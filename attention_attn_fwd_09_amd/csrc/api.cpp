@@ -314,6 +314,9 @@ const char* attn_status_string(attn_status s) {
     case ATTN_ERR_ALIAS: return "an output overlaps an input or another output";
     case ATTN_ERR_UNSUPPORTED: return "valid but unsupported problem (head_dim must be 64 or 128; sizes beyond the 32-bit slice limit; backward needs bf16)";
     case ATTN_ERR_HIP: return "the HIP runtime reported an error";
+    case ATTN_ERR_TOO_LARGE:
+      return "the problem's backward workspace exceeds the fixed scratch array of attn_bwd_noalloc "
+             "(attn_bwd_noalloc_scratch_bytes); call attn_bwd with a workspace instead";
   }
   return "unknown status";
 }

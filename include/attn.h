@@ -34,15 +34,22 @@
  *    default stream) and return without synchronising. Outputs are valid once
  *    the stream reaches that point; inputs must stay unchanged until then.
  *    No host<->device copies happen inside a call.
- *  - Ownership: the library never allocates, frees or retains device memory.
- *    Scratch space is the caller-provided `workspace`, sized by the matching
- *    *_workspace_bytes query (the planner's item list lives there).
- *  - Errors: all argument checks run on the host before any GPU call; on an
- *    error nothing is launched and nothing is written. Device-resident mask
- *    data cannot be checked on the host: padding lengths are clamped to
+ *  - Ownership: the library never allocates or frees device memory. Scratch
+ *    space is the caller-provided `workspace`, sized by the matching
+ *    *_workspace_bytes query (the planner's item list lives there); the one
+ *    exception, attn_bwd_noalloc, uses a fixed array inside the library.
+ *  - Errors: all argument checks run on the host before any launch or memory
+ *    access (the only HIP calls before them are device-attribute queries);
+ *    on an error nothing is launched and nothing is written. Device-resident
+ *    mask data cannot be checked on the host: padding lengths are clamped to
  *    [0, seq] by the kernels. A failed launch returns ATTN_ERR_HIP.
- *  - Thread safety: calls may be issued from several host threads; the only
- *    state is the set of loaded kernels.
+ *  - Device: calls run on the calling thread's current HIP device. Its
+ *    compute-unit and XCD counts are queried once and select the split-KV
+ *    choice and the per-XCD order of work items.
+ *  - Thread safety: calls may be issued from several host threads; the state
+ *    is the set of loaded kernels, the per-device counts above and the
+ *    scratch array of attn_bwd_noalloc (whose calls must not overlap on one
+ *    device).
  */
 #ifndef LIBATTN_ATTN_H
 #define LIBATTN_ATTN_H
@@ -64,7 +71,8 @@ typedef enum {
   ATTN_ERR_WORKSPACE = 6,   /* workspace smaller than the *_workspace_bytes query, or NULL when non-zero is needed */
   ATTN_ERR_ALIAS = 7,       /* an output range overlaps an input range or another output */
   ATTN_ERR_UNSUPPORTED = 8, /* valid but not implemented: head_dim other than 64/128, or an unsupported combination */
-  ATTN_ERR_HIP = 9          /* the HIP runtime reported an error when launching */
+  ATTN_ERR_HIP = 9,         /* the HIP runtime reported an error when launching */
+  ATTN_ERR_TOO_LARGE = 10   /* attn_bwd_noalloc: the problem needs more scratch than its fixed array holds */
 } attn_status;
 
 /* Element types. ATTN_FP8_E4M3 (OCP e4m3, 1 byte) is a forward input type: Q, K, V are fp8,
@@ -201,6 +209,25 @@ attn_status attn_bwd_ex(const attn_problem *problem, const void *Q, const void *
 
 /* Workspace bytes of attn_bwd_ex with these flags (0 for an invalid problem or flag). */
 size_t attn_bwd_ex_workspace_bytes(const attn_problem *problem, const attn_mask *mask, int32_t flags);
+
+/*
+ * Backward that allocates nothing, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation. Same arguments, outputs and
+ * kernels as attn_bwd (two passes, deterministic, results bitwise equal to attn_bwd's) minus the
+ * workspace: the scratch lives in a fixed device array of attn_bwd_noalloc_scratch_bytes() bytes
+ * (32 MiB) inside the library, one copy per device, held until the process ends. A problem whose
+ * attn_bwd_workspace_bytes() exceeds that returns ATTN_ERR_TOO_LARGE before any GPU call; other
+ * errors are as for attn_bwd. Calls on one device share its array, so calls that overlap in time
+ * on one device (other streams or host threads) race; calls ordered on one stream are safe. The
+ * array's address on a device is looked up on the first call on that device (a symbol query, no
+ * allocation); no call allocates or frees memory.
+ */
+attn_status attn_bwd_noalloc(const attn_problem *problem, const void *Q, const void *K, const void *V,
+                             const void *O, const void *dO, const float *LSE, const attn_mask *mask, float scale,
+                             void *dQ, void *dK, void *dV, void *stream);
+
+/* Size in bytes of the fixed scratch array attn_bwd_noalloc uses on each device. */
+size_t attn_bwd_noalloc_scratch_bytes(void);
 
 /*
  * Kernel timing hook, for profiling tools. Kernel classes: */

@@ -54,7 +54,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     lib = _lib()
-    for code in range(10):
+    for code in range(11):
         s = lib.attn_status_string(code).decode()
         assert s and s != "unknown status"
     assert lib.attn_status_string(99).decode() == "unknown status"
