@@ -573,6 +573,338 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdParams p) {
 }
 
 // ------------------------------------------------------------------------------------------------
+// dK/dV pass with wave pairs (two-pass mode). One workgroup per 64-key tile, four waves: two pairs
+// of 32 keys. In a pair, the P wave computes S = Q K^T (its accumulator starts at -LSE / scale, so
+// P = exp2(scale log2(e) acc)), P, and dV += P^T dO; the dP wave computes dP - Delta = dO V^T (its
+// accumulator starts at -Delta), then dS = P (dP - Delta) with the P it receives through LDS, and
+// dK += dS^T Q. Each wave holds only K or V fragments and one accumulator, half of what a wave
+// doing all four products needs, so two waves share each SIMD and cover each other's latencies.
+// No product is computed twice; P crosses once per step, as bf16 (4 KiB per pair).
+// A step is one 64-row query tile of one query head of the group: copy barrier, P-wave scores and
+// exponentials (dP-wave scores alongside), exchange barrier, then the two gradient products.
+template <int D>
+struct PairLds {
+  static constexpr int TILE = BQ * D * 2;
+  static constexpr int STATS = 256;          // 64 row values
+  static constexpr int XCH = 4096;           // one pair's P: [query block][half][lane] x 16 bytes
+  static constexpr int MAX_STEPS = 2048;     // listed (query head, layout row) pairs for block masks
+};
+
+template <int D, int MASK, int MINW>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MINW))) void bwd_dkdv_pair_kernel(BwdParams p) {
+  constexpr int NW = 4;
+  constexpr int BK = 64;        // keys per workgroup
+  constexpr int KS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int RB = D * 2;
+  using L = PairLds<D>;
+  __shared__ __attribute__((aligned(16))) char q_st0[L::TILE];
+  __shared__ __attribute__((aligned(16))) char o_st0[L::TILE];   // dO
+  __shared__ __attribute__((aligned(16))) char q_st1[L::TILE];
+  __shared__ __attribute__((aligned(16))) char o_st1[L::TILE];
+  __shared__ __attribute__((aligned(16))) char s_st0[L::STATS];  // -LSE / scale
+  __shared__ __attribute__((aligned(16))) char d_st0[L::STATS];  // -Delta
+  __shared__ __attribute__((aligned(16))) char s_st1[L::STATS];
+  __shared__ __attribute__((aligned(16))) char d_st1[L::STATS];
+  __shared__ __attribute__((aligned(16))) char xch[2 * L::XCH];
+  constexpr bool LISTED = MASK == MASK_BLOCK || MASK == MASK_DENSE;
+  __shared__ uint16_t list[LISTED ? L::MAX_STEPS : 1];
+  __shared__ int list_count;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pair = wave >> 1, role = wave & 1;   // role 0: S, P, dV; role 1: dP, dS, dK
+  const int c = lane & 31, hh = lane >> 5;
+  const int dsub = ((lane >> 4) & 1) * 16, i16 = lane & 15;
+
+  const uint32_t item = p.items_kv[blockIdx.x];
+  const int kt = (int)(item % (uint32_t)p.n_ktiles);
+  const int bkv = (int)(item / (uint32_t)p.n_ktiles);
+  const int kvh = bkv % p.heads_kv, b = bkv / p.heads_kv;
+  const int k0 = kt * BK;
+  const int kp0 = k0 + pair * 32;   // this pair's keys
+  const int my_k = kp0 + c;
+
+  const size_t kv_off = ((size_t)(b * p.heads_kv + kvh) * p.seq_k) * D;
+  // K rows (P wave) or V rows (dP wave) of this lane's key: B operand of S = Q K^T or dP = dO V^T
+  const __amdgpu_buffer_rsrc_t rf =
+      make_rsrc((const bf16*)(role == 0 ? p.k : p.v) + kv_off, (uint32_t)p.seq_k * RB);
+  bf16x8 frag[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    frag[ks] = __builtin_bit_cast(
+        bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rf, (uint32_t)my_k * RB + (uint32_t)(ks * 32 + hh * 16), 0, 0));
+
+  // ---- the (query head, query tile) steps that see this key tile ----
+  int kv_len = p.seq_k, q_len = p.seq_q;
+  const int n_qt = (p.seq_q + BQ - 1) / BQ;
+  int qt_lo = 0, qt_hi = n_qt;
+  if constexpr (MASK == MASK_PADDING) {
+    kv_len = clamp_len(p.lengths[b], p.seq_k);
+    q_len = clamp_len(p.lengths[b], p.seq_q);
+    qt_hi = (k0 < kv_len) ? (q_len + BQ - 1) / BQ : 0;
+  } else if constexpr (MASK == MASK_CAUSAL) {
+    qt_lo = k0 / BQ;
+  }
+  const bool key_tail = k0 + BK > kv_len;    // some key of the tile is past the end
+  // query tiles [qt_m, qt_f) need no mask; [qt_lo, qt_m) (causal diagonal) and the ragged last
+  // tile [qt_f, qt_hi) do
+  int qt_m = qt_lo, qt_f = qt_hi;
+  if constexpr (MASK == MASK_CAUSAL) qt_m = min(qt_hi, max(qt_lo, (k0 + BK - 2) / BQ + 1));
+  if (qt_hi > qt_m && (qt_hi * BQ > q_len)) qt_f = qt_hi - 1;
+  if (key_tail) qt_f = qt_m;                 // every step masked
+  qt_f = max(qt_f, qt_m);
+  int n_free, n_steps;
+  if constexpr (LISTED) {
+    const int col = k0 / 64;
+    if (wave == 0) {
+      int count = 0;
+      for (int g = 0; g < p.group; ++g) {
+        const uint8_t* lay = p.layout + b * p.layout_stride_b + (kvh * p.group + g) * p.layout_stride_h;
+        for (int r0 = 0; r0 < p.nb_q; r0 += 64) {
+          const int r = r0 + lane;
+          const bool keep = r < p.nb_q && lay[(size_t)r * p.nb_k + col] != 0;
+          const uint64_t ball = __ballot(keep);
+          const int before = __builtin_amdgcn_mbcnt_hi((uint32_t)(ball >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ball, 0));
+          if (keep && count + before < L::MAX_STEPS) list[count + before] = (uint16_t)((g << 10) | r);
+          count += __popcll(ball);
+        }
+      }
+      if (lane == 0) list_count = min(count, L::MAX_STEPS);
+    }
+    lds_barrier();   // the fragment loads issued above stay in flight
+    n_steps = list_count;
+    // ragged shapes run every step through the masked body, and so does a dense mask
+    n_free = (MASK == MASK_DENSE || key_tail || (p.seq_q % BQ) != 0) ? 0 : n_steps;
+  } else {
+    n_free = p.group * (qt_f - qt_m);
+    n_steps = p.group * (qt_hi - qt_lo);
+  }
+  auto step_at = [&](int s, int& g, int& qt) __attribute__((always_inline)) {
+    if constexpr (LISTED) {
+      const uint32_t e = list[s];
+      g = (int)(e >> 10);
+      qt = (int)(e & 1023u);
+    } else {
+      if (s < n_free) {
+        const int per = qt_f - qt_m;
+        g = s / per;
+        qt = qt_m + s % per;
+      } else {
+        const int r = s - n_free;
+        const int per = (qt_m - qt_lo) + (qt_hi - qt_f);
+        g = r / per;
+        const int m = r % per;
+        qt = m < qt_m - qt_lo ? qt_lo + m : qt_f + (m - (qt_m - qt_lo));
+      }
+    }
+  };
+
+  auto issue_step = [&](auto stage_tag, int s) __attribute__((always_inline)) {
+    constexpr int ST = decltype(stage_tag)::value;
+    int g, qt;
+    step_at(s, g, qt);
+    const int hq = kvh * p.group + g;
+    const size_t q_off = ((size_t)(b * p.heads_q + hq) * p.seq_q) * D;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc((const bf16*)p.q + q_off, (uint32_t)p.seq_q * RB);
+    const __amdgpu_buffer_rsrc_t rdo = make_rsrc((const bf16*)p.dout + q_off, (uint32_t)p.seq_q * RB);
+    issue_rows<D, NW>(ST == 0 ? q_st0 : q_st1, rq, qt * BQ, wave, lane);
+    issue_rows<D, NW>(ST == 0 ? o_st0 : o_st1, rdo, qt * BQ, wave, lane);
+    if (wave == 0 && lane < 16) {
+      // 64 row values; rows past the sequence read as 0 (their steps run the masked body)
+      const size_t r_off = (size_t)(b * p.heads_q + hq) * p.seq_q;
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.sseed + r_off, (uint32_t)p.seq_q * 4);
+      const __amdgpu_buffer_rsrc_t rd = make_rsrc(p.delta + r_off, (uint32_t)p.seq_q * 4);
+      const uint32_t off = (uint32_t)(qt * BQ + lane * 4) * 4;
+      buffer_to_lds16(rs, ST == 0 ? s_st0 : s_st1, off);
+      buffer_to_lds16(rd, ST == 0 ? d_st0 : d_st1, off);
+    }
+  };
+
+  // per-lane LDS offsets inside a 64-row Q/dO tile: row fragments of query block qb (rows
+  // qb*32 + sigma32(c)) and transposed fragments (rows qb*32 + hh*16 + hc*8 + 0..7)
+  int roff[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) roff[ks] = sigma32(c) * RB + (((2 * ks + hh) ^ swz<D>(sigma32(c))) * 16);
+  int toff[DB][2];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int row = hh * 16 + half * 4 + (i16 >> 2);
+      const int d = db * 32 + dsub + 4 * (i16 & 3);
+      toff[db][half] = row * RB + (((d >> 3) ^ swz<D>(row)) * 16) + (d & 7) * 2;
+    }
+  }
+  // this pair's P exchange tile; lane-linear 16-byte chunks, so writes and reads are conflict free
+  char* xp = xch + pair * L::XCH + lane * 16;
+
+  // dense mask: bits of the step's queries q0 .. q0+63 for this lane's key and the step's query
+  // head (0 past the key range), two words; loaded one step ahead of the step that tests them
+  auto dcol_words = [&](int s, uint32_t (&w)[2]) __attribute__((always_inline)) {
+    int g, qt;
+    step_at(s, g, qt);
+    const uint32_t* dcol = p.dense.cols + b * p.dense.cols_stride_b + (kvh * p.group + g) * p.dense.cols_stride_h +
+                           (int64_t)min(my_k, p.seq_k - 1) * p.dense.col_words;
+    dense_words(dcol, my_k < p.seq_k, p.dense.col_words, qt * BQ, w);
+  };
+
+  f32x16 acc[DB];   // dV (P wave) or dK / scale (dP wave) of this pair's 32 keys
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+  const float cs = p.scale_log2;
+
+  // 16 row values of query block qb in MFMA accumulator order (queries qb*32 + hh*16 + 0..15)
+  auto stats16 = [&](const char* st, int qb) __attribute__((always_inline)) -> f32x16 {
+    f32x16 r;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const f32x4 v = *(const f32x4*)(st + (qb * 32 + hh * 16 + 4 * k) * 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[4 * k + e] = v[e];
+    }
+    return r;
+  };
+  // the two 32-query blocks' accumulators seeded from `st`, then += rows(tile) x frag^T (two
+  // interleaved MFMA chains)
+  auto scores = [&](const char* tile, const char* st, f32x16 (&a)[2]) __attribute__((always_inline)) {
+    a[0] = stats16(st, 0);
+    a[1] = stats16(st, 1);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 x0 = *(const bf16x8*)(tile + roff[ks]);
+      const bf16x8 x1 = *(const bf16x8*)(tile + roff[ks] + 32 * RB);
+      a[0] = mfma32(x0, frag[ks], a[0]);
+      a[1] = mfma32(x1, frag[ks], a[1]);
+    }
+  };
+  // acc += A^T B over the step's 64 queries: A = this lane's bf16 operand of (query block qb, chunk
+  // hc), B = transposed fragments of `tile` (rows qb*32 + hh*16 + hc*8 + 0..7)
+  auto grads = [&](const char* tile, const bf16x8 (&a)[2][2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int hc = 0; hc < 2; ++hc) {
+        const int rows = (qb * 32 + hc * 8) * RB;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, tile + toff[db][0] + rows));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, tile + toff[db][1] + rows));
+          acc[db] = mfma32(a[qb][hc], __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)),
+                           acc[db]);
+        }
+      }
+    }
+  };
+
+  uint32_t dcur[2] = {0u, 0u}, dnext[2] = {0u, 0u};
+
+  // One step of the P wave (ROLE 0) or the dP wave (ROLE 1). Every wave passes both barriers of
+  // every step; a pair whose keys see none of the step's queries skips its products.
+  auto step = [&](auto role_tag, auto stage_tag, auto masked_tag, int s) __attribute__((always_inline)) {
+    constexpr int ROLE = decltype(role_tag)::value;
+    constexpr int ST = decltype(stage_tag)::value;
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const char* ql = ST == 0 ? q_st0 : q_st1;
+    const char* dol = ST == 0 ? o_st0 : o_st1;
+    wait_vmem();
+    __syncthreads();   // step s is in LDS; every wave is done with the stage step s+1 overwrites
+    if (s + 1 < n_steps) issue_step(std::integral_constant<int, 1 - ST>{}, s + 1);
+    int g, qt;
+    step_at(s, g, qt);
+    const int q0 = qt * BQ;
+    if constexpr (ROLE == 0 && MASK == MASK_DENSE) {
+      dcur[0] = dnext[0];
+      dcur[1] = dnext[1];
+      if (s + 1 < n_steps) dcol_words(s + 1, dnext);
+    }
+    bool active = true;
+    if constexpr (MASKED) {
+      active = kp0 < kv_len;
+      if constexpr (MASK == MASK_CAUSAL) active = active && kp0 <= q0 + BQ - 1;
+      if constexpr (MASK == MASK_PADDING) active = active && q0 < q_len;
+    }
+    if constexpr (ROLE == 0) {
+      bf16x8 pb[2][2];
+      if (active) {
+        f32x16 sc[2];
+        scores(ql, ST == 0 ? s_st0 : s_st1, sc);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            float pv = fast_exp2(sc[qb][i] * cs);
+            if constexpr (MASKED) {
+              const int q = q0 + qb * 32 + hh * 16 + i;
+              bool vis = q < q_len && my_k < kv_len;
+              if constexpr (MASK == MASK_CAUSAL) vis = vis && my_k <= q;
+              if constexpr (MASK == MASK_DENSE) vis = vis && ((dcur[qb] >> (hh * 16 + i)) & 1u);
+              pv = vis ? pv : 0.0f;
+            }
+            pb[qb][i >> 3][i & 7] = (bf16)pv;
+          }
+          *(bf16x8*)(xp + qb * 2048) = pb[qb][0];
+          *(bf16x8*)(xp + qb * 2048 + 1024) = pb[qb][1];
+        }
+      }
+      lds_barrier();   // P is in LDS for the dP wave
+      if (active) grads(dol, pb);   // dV += P^T dO
+    } else {
+      f32x16 dp[2];
+      if (active) scores(dol, ST == 0 ? d_st0 : d_st1, dp);   // dP - Delta
+      lds_barrier();
+      if (active) {
+        bf16x8 dsb[2][2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const bf16x8 p0 = *(const bf16x8*)(xp + qb * 2048);
+          const bf16x8 p1 = *(const bf16x8*)(xp + qb * 2048 + 1024);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            dsb[qb][0][i] = (bf16)((float)p0[i] * dp[qb][i]);
+            dsb[qb][1][i] = (bf16)((float)p1[i] * dp[qb][8 + i]);
+          }
+        }
+        grads(ql, dsb);   // dK += dS^T Q
+      }
+    }
+  };
+  auto run_role = [&](auto role_tag) __attribute__((always_inline)) {
+    auto run = [&](auto masked_tag, int s0, int s1) __attribute__((always_inline)) {
+      int s = s0;
+      if (s < s1 && (s & 1)) step(role_tag, std::integral_constant<int, 1>{}, masked_tag, s++);
+      for (; s + 1 < s1; s += 2) {
+        step(role_tag, std::integral_constant<int, 0>{}, masked_tag, s);
+        step(role_tag, std::integral_constant<int, 1>{}, masked_tag, s + 1);
+      }
+      if (s < s1) step(role_tag, std::integral_constant<int, 0>{}, masked_tag, s);
+    };
+    run(std::false_type{}, 0, n_free);
+    run(std::true_type{}, n_free, n_steps);
+  };
+
+  if constexpr (MASK == MASK_DENSE)
+    if (role == 0 && n_steps > 0) dcol_words(0, dnext);
+  if (n_steps > 0) issue_step(std::integral_constant<int, 0>{}, 0);
+  if (role == 0) run_role(std::integral_constant<int, 0>{});
+  else run_role(std::integral_constant<int, 1>{});
+
+  // ---- write dV (P wave) or dK = scale * acc (dP wave); lane (c, hh) holds column db*32 + c of
+  // keys kp0 + (i / 4) * 8 + hh * 4 + i % 4 ----
+  bf16* out = (bf16*)(role == 0 ? p.dv : p.dk) + kv_off;
+  const float f = role == 0 ? 1.0f : p.scale;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = kp0 + (i >> 2) * 8 + hh * 4 + (i & 3);
+      if (key < p.seq_k) out[(size_t)key * D + db * 32 + c] = (bf16)(acc[db][i] * f);
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
 // dQ pass: same tile loop as the forward kernel (K and V tiles double-buffered in four separately
 // named LDS arrays, per-lane precomputed swizzled offsets, mask-free tiles in their own loop).
 template <int D>
@@ -684,6 +1016,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
   if (row_ok && hh == 0) {
     p.delta[row_off + my_q] = ndelta;
     p.lse2[row_off + my_q] = lse2;
+    // the wave-pair dK/dV pass starts its score accumulator at -LSE / scale (-inf for empty rows)
+    if (p.sseed != nullptr) p.sseed[row_off + my_q] = -lse2 * p.inv_scale_log2;
   }
 
   // per-lane LDS offsets: row fragments (K and V tiles share the layout) and transposed K reads
@@ -858,6 +1192,23 @@ hipError_t launch_dq_one(const BwdParams& p, int n_items, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int D, int MASK>
+hipError_t launch_pair_one(const BwdParams& p, int n_items, hipStream_t s) {
+  hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D, MASK, 2>), dim3(n_items), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t dkdv_pair_mask(const BwdParams& p, int mask, int n_items, hipStream_t s) {
+  switch (mask) {
+    case MASK_NONE: return launch_pair_one<D, MASK_NONE>(p, n_items, s);
+    case MASK_CAUSAL: return launch_pair_one<D, MASK_CAUSAL>(p, n_items, s);
+    case MASK_PADDING: return launch_pair_one<D, MASK_PADDING>(p, n_items, s);
+    case MASK_DENSE: return launch_pair_one<D, MASK_DENSE>(p, n_items, s);
+    default: return launch_pair_one<D, MASK_BLOCK>(p, n_items, s);
+  }
+}
+
 template <int D>
 hipError_t dkdv_mask(const BwdParams& p, int mask, int n_items, hipStream_t s) {
   if (p.dq_acc != nullptr) {
@@ -909,9 +1260,14 @@ hipError_t dq_mask(const BwdParams& p, int mask, int n_items, hipStream_t s) {
 // union of their kept tiles and each wave pair computes only its own row's). dK/dV items are 128
 // keys, or one 64-key layout column for block masks (2 waves).
 int bwd_block_q(int head_dim, int mask) { (void)head_dim; (void)mask; return 128; }
-int bwd_block_k(int head_dim, int mask) {
+bool bwd_pair_kernel(int mask, int flags, int group, int nb_q) {
+  if (flags != 0) return false;
+  if (mask == MASK_BLOCK || mask == MASK_DENSE) return (int64_t)group * nb_q <= PairLds<128>::MAX_STEPS;
+  return true;
+}
+int bwd_block_k(int head_dim, int mask, bool pair_kernel) {
   (void)head_dim;
-  return (mask == MASK_BLOCK || mask == MASK_DENSE) ? 64 : 128;
+  return (pair_kernel || mask == MASK_BLOCK || mask == MASK_DENSE) ? 64 : 128;
 }
 int bwd_max_steps() { return KvLds<128>::MAX_STEPS; }
 
@@ -927,6 +1283,10 @@ hipError_t launch_bwd_preprocess(const BwdParams& p, int head_dim, hipStream_t s
 
 hipError_t launch_bwd_dkdv(const BwdParams& p, int head_dim, int mask, int n_items, hipStream_t s) {
   return head_dim == 128 ? dkdv_mask<128>(p, mask, n_items, s) : dkdv_mask<64>(p, mask, n_items, s);
+}
+
+hipError_t launch_bwd_dkdv_pair(const BwdParams& p, int head_dim, int mask, int n_items, hipStream_t s) {
+  return head_dim == 128 ? dkdv_pair_mask<128>(p, mask, n_items, s) : dkdv_pair_mask<64>(p, mask, n_items, s);
 }
 
 hipError_t launch_bwd_dq(const BwdParams& p, int head_dim, int mask, int n_items, hipStream_t s) {

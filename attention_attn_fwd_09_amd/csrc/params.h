@@ -59,6 +59,8 @@ struct BwdParams {
   void* dv;
   float* delta;                 // workspace: -rowsum(dO * O) (negated Delta), fp32 [B, Hq, Sq]
   float* lse2;                  // workspace: LSE * log2(e), +inf for empty rows, fp32 [B, Hq, Sq]
+  float* sseed;                 // workspace (two-pass mode): -LSE / scale, -inf for empty rows, fp32
+                                //   [B, Hq, Sq]: the start value of the dK/dV pass's score accumulator
   DenseBits dense;              // MASK_DENSE
   float* dq_acc;                // single-pass mode: dQ / scale accumulated with fp32 atomics,
                                 //   [B, Hq, Sq, D]; zeroed by the preprocess; null otherwise
@@ -72,6 +74,7 @@ struct BwdParams {
   int32_t n_qtiles, n_ktiles;
   int32_t nb_q, nb_k;
   float scale, scale_log2;
+  float inv_scale_log2;         // 1 / scale_log2
 };
 
 }  // namespace attn

