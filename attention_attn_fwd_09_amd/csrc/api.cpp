@@ -236,7 +236,7 @@ attn_status check_splits(const attn_problem* p, const attn_mask* m, int32_t requ
 }
 
 struct BwdSizes {
-  bool pair;   // wave-pair dK/dV kernel
+  int dkdv;    // dK/dV kernel variant (DKDV_*)
   int bq, bk, n_qt, n_kt;
   int64_t q_items, kv_items;
   size_t delta_off, lse2_off, sseed_off, kv_off, q_off, dq_acc_off, dense_off, total;
@@ -247,9 +247,9 @@ struct BwdSizes {
 // -Delta, LSE*log2(e), dK/dV items, then the fp32 dQ accumulator [B, Hq, Sq, D].
 BwdSizes bwd_sizes(const attn_problem* p, const attn_mask* m, int32_t flags = 0) {
   BwdSizes s;
-  s.pair = bwd_pair_kernel(m->kind, flags, p->heads_q / p->heads_kv, ceil_div(p->seq_q, 64));
+  s.dkdv = bwd_dkdv_variant(m->kind, flags, p->heads_q / p->heads_kv, ceil_div(p->seq_q, 64));
   s.bq = bwd_block_q(p->head_dim, m->kind);
-  s.bk = bwd_block_k(p->head_dim, m->kind, s.pair);
+  s.bk = bwd_block_k(p->head_dim, m->kind, s.dkdv);
   s.n_qt = ceil_div(p->seq_q, s.bq);
   s.n_kt = ceil_div(p->seq_k, s.bk);
   s.q_items = (int64_t)p->batch * p->heads_q * s.n_qt;
@@ -257,7 +257,7 @@ BwdSizes bwd_sizes(const attn_problem* p, const attn_mask* m, int32_t flags = 0)
   s.delta_off = 0;
   s.lse2_off = align_up((size_t)p->batch * p->heads_q * p->seq_q * 4);
   s.sseed_off = s.lse2_off + align_up((size_t)p->batch * p->heads_q * p->seq_q * 4);
-  s.kv_off = s.sseed_off + (s.pair ? align_up((size_t)p->batch * p->heads_q * p->seq_q * 4) : 0);
+  s.kv_off = s.sseed_off + (s.dkdv != DKDV_ONE_WAVE ? align_up((size_t)p->batch * p->heads_q * p->seq_q * 4) : 0);
   s.q_off = s.kv_off + align_up((size_t)s.kv_items * 4);
   if (flags & ATTN_BWD_ATOMIC_DQ) {
     s.dq_acc_off = s.q_off;
@@ -569,7 +569,7 @@ attn_status bwd_call(const attn_problem* problem, const void* Q, const void* K, 
   bp.dq = dQ; bp.dk = dK; bp.dv = dV;
   bp.delta = (float*)(ws + bs.delta_off);
   bp.lse2 = (float*)(ws + bs.lse2_off);
-  bp.sseed = bs.pair ? (float*)(ws + bs.sseed_off) : nullptr;
+  bp.sseed = bs.dkdv != DKDV_ONE_WAVE ? (float*)(ws + bs.sseed_off) : nullptr;
   bp.lengths = m->lengths; bp.layout = m->block_layout;
   bp.layout_stride_b = m->layout_stride_b; bp.layout_stride_h = m->layout_stride_h;
   bp.items_kv = (const uint32_t*)(ws + bs.kv_off);
@@ -627,8 +627,8 @@ attn_status bwd_call(const attn_problem* problem, const void* Q, const void* K, 
       timed(ATTN_KERNEL_BWD_DQ, s, [&] { return launch_bwd_dq(bp, p->head_dim, m->kind, (int)bs.q_items, s); }));
   if (st != ATTN_OK) return st;
   return hip_status(timed(ATTN_KERNEL_BWD_DKDV, s, [&] {
-    return bs.pair ? launch_bwd_dkdv_pair(bp, p->head_dim, m->kind, (int)bs.kv_items, s)
-                   : launch_bwd_dkdv(bp, p->head_dim, m->kind, (int)bs.kv_items, s);
+    if (bs.dkdv == DKDV_PAIR) return launch_bwd_dkdv_pair(bp, p->head_dim, m->kind, (int)bs.kv_items, s);
+    return launch_bwd_dkdv(bp, p->head_dim, m->kind, (int)bs.kv_items, s);
   }));
 }
 

@@ -611,12 +611,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MINW))) voi
   __shared__ uint16_t list[LISTED ? L::MAX_STEPS : 1];
   __shared__ int list_count;
 
+  __shared__ int simd_of[NW];
+
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int pair = wave >> 1, role = wave & 1;   // role 0: S, P, dV; role 1: dP, dS, dK
   const int c = lane & 31, hh = lane >> 5;
   const int dsub = ((lane >> 4) & 1) * 16, i16 = lane & 15;
+
+  // Pair and role of this wave. A CU holds two of these workgroups (workgroup slots 0 and 1), and
+  // the four waves of each spread over the four SIMDs. Ranking the waves by SIMD and flipping the
+  // role with the slot's parity puts one P wave and one dP wave on every SIMD, so the exponentials
+  // of one run under the MFMAs of the other. Any placement gives a valid assignment: the ranks are
+  // a permutation, and each pair gets one wave of each role.
+  const uint32_t hw_id = __builtin_amdgcn_s_getreg((31 << 11) | 4);   // HW_REG_HW_ID
+  const int my_simd = (int)((hw_id >> 4) & 3), slot = (int)((hw_id >> 16) & 1);
+  if (lane == 0) simd_of[wave] = my_simd;
+  lds_barrier();
+  int rank = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int sw = simd_of[w];
+    rank += (sw < my_simd || (sw == my_simd && w < wave)) ? 1 : 0;
+  }
+  rank = __builtin_amdgcn_readfirstlane(rank);
+  const int pair = rank >> 1, role = (rank & 1) ^ slot;   // role 0: S, P, dV; role 1: dP, dS, dK
 
   const uint32_t item = p.items_kv[blockIdx.x];
   const int kt = (int)(item % (uint32_t)p.n_ktiles);
@@ -779,21 +798,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MINW))) voi
       a[1] = mfma32(x1, frag[ks], a[1]);
     }
   };
-  // acc += A^T B over the step's 64 queries: A = this lane's bf16 operand of (query block qb, chunk
-  // hc), B = transposed fragments of `tile` (rows qb*32 + hh*16 + hc*8 + 0..7)
-  auto grads = [&](const char* tile, const bf16x8 (&a)[2][2]) __attribute__((always_inline)) {
+  // acc += A^T B over the 32 queries of block qb: A = this lane's bf16 operand of chunk hc, B =
+  // transposed fragments of `tile` (rows qb*32 + hh*16 + hc*8 + 0..7)
+  auto grads = [&](const char* tile, int qb, const bf16x8 (&a)[2]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int hc = 0; hc < 2; ++hc) {
+      const int rows = (qb * 32 + hc * 8) * RB;
 #pragma unroll
-      for (int hc = 0; hc < 2; ++hc) {
-        const int rows = (qb * 32 + hc * 8) * RB;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, tile + toff[db][0] + rows));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, tile + toff[db][1] + rows));
-          acc[db] = mfma32(a[qb][hc], __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)),
-                           acc[db]);
-        }
+      for (int db = 0; db < DB; ++db) {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, tile + toff[db][0] + rows));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, tile + toff[db][1] + rows));
+        acc[db] = mfma32(a[hc], __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)),
+                         acc[db]);
       }
     }
   };
@@ -825,48 +841,54 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MINW))) voi
       if constexpr (MASK == MASK_CAUSAL) active = active && kp0 <= q0 + BQ - 1;
       if constexpr (MASK == MASK_PADDING) active = active && q0 < q_len;
     }
+    // P crosses one 32-query block at a time (one barrier per block), so that the P wave's
+    // exponentials of block 1 run under its own dV products of block 0 and the dP wave starts on
+    // block 0 half a step earlier.
     if constexpr (ROLE == 0) {
-      bf16x8 pb[2][2];
-      if (active) {
-        f32x16 sc[2];
-        scores(ql, ST == 0 ? s_st0 : s_st1, sc);
+      f32x16 sc[2];
+      if (active) scores(ql, ST == 0 ? s_st0 : s_st1, sc);
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+      for (int qb = 0; qb < 2; ++qb) {
+        bf16x8 pb[2];
+        if (active) {
+          float pv[16];
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            float pv = fast_exp2(sc[qb][i] * cs);
+            pv[i] = fast_exp2(sc[qb][i] * cs);
             if constexpr (MASKED) {
               const int q = q0 + qb * 32 + hh * 16 + i;
               bool vis = q < q_len && my_k < kv_len;
               if constexpr (MASK == MASK_CAUSAL) vis = vis && my_k <= q;
               if constexpr (MASK == MASK_DENSE) vis = vis && ((dcur[qb] >> (hh * 16 + i)) & 1u);
-              pv = vis ? pv : 0.0f;
+              pv[i] = vis ? pv[i] : 0.0f;
             }
-            pb[qb][i >> 3][i & 7] = (bf16)pv;
           }
-          *(bf16x8*)(xp + qb * 2048) = pb[qb][0];
-          *(bf16x8*)(xp + qb * 2048 + 1024) = pb[qb][1];
+          pb[0] = pack_bf16x8(pv);
+          pb[1] = pack_bf16x8(pv + 8);
+          *(bf16x8*)(xp + qb * 2048) = pb[0];
+          *(bf16x8*)(xp + qb * 2048 + 1024) = pb[1];
         }
+        lds_barrier();   // P of block qb is in LDS for the dP wave
+        if (active) grads(dol, qb, pb);   // dV += P^T dO
       }
-      lds_barrier();   // P is in LDS for the dP wave
-      if (active) grads(dol, pb);   // dV += P^T dO
     } else {
       f32x16 dp[2];
       if (active) scores(dol, ST == 0 ? d_st0 : d_st1, dp);   // dP - Delta
-      lds_barrier();
-      if (active) {
-        bf16x8 dsb[2][2];
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+      for (int qb = 0; qb < 2; ++qb) {
+        lds_barrier();
+        if (active) {
           const bf16x8 p0 = *(const bf16x8*)(xp + qb * 2048);
           const bf16x8 p1 = *(const bf16x8*)(xp + qb * 2048 + 1024);
+          float ds[16];
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
-            dsb[qb][0][i] = (bf16)((float)p0[i] * dp[qb][i]);
-            dsb[qb][1][i] = (bf16)((float)p1[i] * dp[qb][8 + i]);
+            ds[i] = (float)p0[i] * dp[qb][i];
+            ds[8 + i] = (float)p1[i] * dp[qb][8 + i];
           }
+          const bf16x8 dsb[2] = {pack_bf16x8(ds), pack_bf16x8(ds + 8)};
+          grads(ql, qb, dsb);   // dK += dS^T Q
         }
-        grads(ql, dsb);   // dK += dS^T Q
       }
     }
   };
@@ -1260,14 +1282,17 @@ hipError_t dq_mask(const BwdParams& p, int mask, int n_items, hipStream_t s) {
 // union of their kept tiles and each wave pair computes only its own row's). dK/dV items are 128
 // keys, or one 64-key layout column for block masks (2 waves).
 int bwd_block_q(int head_dim, int mask) { (void)head_dim; (void)mask; return 128; }
-bool bwd_pair_kernel(int mask, int flags, int group, int nb_q) {
-  if (flags != 0) return false;
-  if (mask == MASK_BLOCK || mask == MASK_DENSE) return (int64_t)group * nb_q <= PairLds<128>::MAX_STEPS;
-  return true;
+int bwd_dkdv_variant(int mask, int flags, int group, int nb_q) {
+  if (flags != 0) return DKDV_ONE_WAVE;
+  if ((mask == MASK_BLOCK || mask == MASK_DENSE) && (int64_t)group * nb_q > PairLds<128>::MAX_STEPS)
+    return DKDV_ONE_WAVE;
+  return DKDV_PAIR;
 }
-int bwd_block_k(int head_dim, int mask, bool pair_kernel) {
+int bwd_block_k(int head_dim, int mask, int variant) {
   (void)head_dim;
-  return (pair_kernel || mask == MASK_BLOCK || mask == MASK_DENSE) ? 64 : 128;
+  const bool listed = mask == MASK_BLOCK || mask == MASK_DENSE;
+  if (variant == DKDV_PAIR || listed) return 64;
+  return 128;
 }
 int bwd_max_steps() { return KvLds<128>::MAX_STEPS; }
 
@@ -1288,6 +1313,7 @@ hipError_t launch_bwd_dkdv(const BwdParams& p, int head_dim, int mask, int n_ite
 hipError_t launch_bwd_dkdv_pair(const BwdParams& p, int head_dim, int mask, int n_items, hipStream_t s) {
   return head_dim == 128 ? dkdv_pair_mask<128>(p, mask, n_items, s) : dkdv_pair_mask<64>(p, mask, n_items, s);
 }
+
 
 hipError_t launch_bwd_dq(const BwdParams& p, int head_dim, int mask, int n_items, hipStream_t s) {
   return head_dim == 128 ? dq_mask<128>(p, mask, n_items, s) : dq_mask<64>(p, mask, n_items, s);

@@ -92,6 +92,21 @@ __device__ __forceinline__ int sigma32(int r) { return ((r >> 2) & 1) * 16 + (r 
 __device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 __device__ __forceinline__ float vmax3(float a, float b, float c) { return vmax(vmax(a, b), c); }
 
+// Eight fp32 values to bf16 (round to nearest even), converted in pairs: four v_cvt_pk_bf16_f32.
+// Storing element by element into a vector makes the compiler convert one value per instruction
+// and merge the halves with extra permutes.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bf16x8 pack_bf16x8(const float* v) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) {
+    const bf16x2 h = __builtin_convertvector((f32x2){v[i], v[i + 1]}, bf16x2);
+    r[i] = h[0];
+    r[i + 1] = h[1];
+  }
+  return r;
+}
+
 // acc + sum of the 8 bf16 values of x, in fp32, four v_dot2 ops against (1, 1)
 __device__ __forceinline__ float sum_bf16x8(bf16x8 x, float acc) {
   const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};

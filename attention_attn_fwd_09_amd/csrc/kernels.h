@@ -58,10 +58,11 @@ hipError_t launch_fwd_f32(const FwdParams& p, int head_dim, int mask, hipStream_
 
 // Backward: tile sizes and launchers.
 int bwd_block_q(int head_dim, int mask);
-// Whether the two-pass backward runs the wave-pair dK/dV kernel (64-key items, two waves per SIMD)
-// for this problem, or the one-wave-per-SIMD kernel (also used by the single-pass mode).
-bool bwd_pair_kernel(int mask, int flags, int group, int nb_q);
-int bwd_block_k(int head_dim, int mask, bool pair_kernel);
+// dK/dV kernel of a backward call: one wave per 32 keys (single-pass mode, and layouts with more
+// listed steps than the wave-pair kernel holds), or wave pairs in 64-key workgroups.
+enum { DKDV_ONE_WAVE = 0, DKDV_PAIR = 1 };
+int bwd_dkdv_variant(int mask, int flags, int group, int nb_q);
+int bwd_block_k(int head_dim, int mask, int variant);
 int bwd_max_steps();  // (query head, query tile) pairs one dK/dV workgroup can list for a block mask
 hipError_t launch_bwd_preprocess(const BwdParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdParams& p, int head_dim, int mask, int n_items, hipStream_t stream);
