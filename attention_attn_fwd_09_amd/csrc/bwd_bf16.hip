@@ -1035,11 +1035,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
   const bool row_ok = my_q < p.seq_q;
   const float lse2 = row_ok ? lse_to_log2(p.lse[row_off + my_q]) : INFINITY;
   const float ndelta = row_ok ? -dsum : 0.0f;   // -Delta
+  const float sseed = -lse2 * p.inv_scale_log2;  // -LSE / scale; -inf for empty rows and rows past the end
   if (row_ok && hh == 0) {
     p.delta[row_off + my_q] = ndelta;
     p.lse2[row_off + my_q] = lse2;
     // the wave-pair dK/dV pass starts its score accumulator at -LSE / scale (-inf for empty rows)
-    if (p.sseed != nullptr) p.sseed[row_off + my_q] = -lse2 * p.inv_scale_log2;
+    if (p.sseed != nullptr) p.sseed[row_off + my_q] = sseed;
   }
 
   // per-lane LDS offsets: row fragments (K and V tiles share the layout) and transposed K reads
@@ -1081,7 +1082,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
     const char* vl = ST == 0 ? v_st0 : v_st1;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      f32x16 sc = f32x16{}, dp = f32x16{};
+      // the score accumulator starts at -LSE / scale and the dP one at -Delta, so that
+      // P = exp2(scale log2(e) acc) and dS = P acc need no per-element offset
+      f32x16 sc, dp;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        sc[i] = sseed;
+        dp[i] = ndelta;
+      }
       bf16x8 ka[KS], va[KS];
       uint32_t dw = 0;
       if constexpr (MASK == MASK_DENSE) {
@@ -1118,10 +1126,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
           kt[hc][db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         }
       }
-      bf16x8 dsb[2];
+      float ds[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float pv = fast_exp2(fmaf(sc[i], cs, -lse2));
+        float pv = fast_exp2(sc[i] * cs);
         if constexpr (MASKED) {
           const int key = k0 + kb * 32 + hh * 16 + i;
           bool vis = key < kv_len && my_q < q_len;
@@ -1129,8 +1137,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
           if constexpr (MASK == MASK_DENSE) vis = vis && ((dw >> (hh * 16 + i)) & 1u);
           pv = vis ? pv : 0.0f;
         }
-        dsb[i >> 3][i & 7] = (bf16)(pv * (dp[i] + ndelta));
+        ds[i] = pv * dp[i];
       }
+      const bf16x8 dsb[2] = {pack_bf16x8(ds), pack_bf16x8(ds + 8)};
 #pragma unroll
       for (int hc = 0; hc < 2; ++hc) {
 #pragma unroll

@@ -144,11 +144,75 @@ __device__ int block_exclusive_scan(int v, int* wave_sums) {
   return wave_sums[wave] + incl - v;
 }
 
+// Closed-form list for a block layout shared by every (batch, head): all units have the same
+// per-tile costs, so the tiles are ranked once (longest first, ties by index) and the list is
+// rank-major, unit-minor, with unit u on XCD u % n_xcd (list positions slot * n_xcd + xcd). The
+// layout is staged in LDS with one coalesced pass; no histogram or scan is needed.
+constexpr int MAX_RANKED = 256;                // tiles ranked in closed form (the ranking is quadratic)
+constexpr int MAX_STAGED_LAYOUT = 2 * MAX_CACHED;   // layout bytes staged in LDS (the `cached` array)
+
+__device__ __forceinline__ bool closed_form_plan(const PlanParams& p) {
+  return p.mask == MASK_BLOCK && p.layout_stride_b == 0 && p.layout_stride_h == 0 && p.tile >= 64 &&
+         p.n_tiles <= MAX_RANKED && (int64_t)p.nb_q * p.nb_k <= MAX_STAGED_LAYOUT;
+}
+
+__device__ __forceinline__ void plan_closed_form(const PlanParams& p, uint8_t* lay, int* cost, int* order) {
+  const int nbytes = p.nb_q * p.nb_k;
+  for (int i = threadIdx.x; i < nbytes; i += THREADS) lay[i] = p.layout[i];
+  for (int t = threadIdx.x; t < p.n_tiles; t += THREADS) cost[t] = 0;
+  __syncthreads();
+  // kept tiles in the union of each tile's layout rows (columns): one (tile, column) pair per thread
+  const int per_unit = p.tile / 64;   // layout rows (query tiles) or columns (key tiles) per tile
+  const int n_other = p.mode == PLAN_BWD_KV ? p.nb_q : p.nb_k;
+  const int pairs = p.n_tiles * n_other;
+  for (int e = threadIdx.x; e < pairs; e += THREADS) {
+    const int t = e / n_other, x = e - t * n_other;
+    bool keep = false;
+    for (int r = 0; r < per_unit; ++r) {
+      const int y = t * per_unit + r;
+      if (p.mode == PLAN_BWD_KV) keep = keep || (y < p.nb_k && lay[x * p.nb_k + y] != 0);
+      else keep = keep || (y < p.nb_q && lay[y * p.nb_k + x] != 0);
+    }
+    if (keep) atomicAdd(&cost[t], 1);
+  }
+  __syncthreads();
+  // rank of each tile, longest first and ties by index: one wave per tile, 64 comparisons a ballot
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int t = wave; t < p.n_tiles; t += THREADS / 64) {
+    const int c = cost[t];
+    int r = 0;
+    for (int u0 = 0; u0 < p.n_tiles; u0 += 64) {
+      const int u = u0 + lane;
+      const bool before = u < p.n_tiles && (cost[u] > c || (cost[u] == c && u < t));
+      r += __popcll(__ballot(before));
+    }
+    if (lane == 0) order[r] = t;
+  }
+  __syncthreads();
+  const int G = p.mode == PLAN_BWD_KV ? 1 : p.group;   // heads per unit
+  const int per_unit_items = G * p.n_tiles;
+  const int n_units = p.n_items / per_unit_items;
+  const int heads_kv = p.heads / G;
+  const int n_xcd = (p.n_xcd > 1 && p.n_xcd <= kMaxXcd && n_units % p.n_xcd == 0) ? p.n_xcd : 1;
+  const int per_rank = (n_units / n_xcd) * G;
+  for (int pos = threadIdx.x; pos < p.n_items; pos += THREADS) {
+    const int x = pos % n_xcd, slot = pos / n_xcd;
+    const int r = slot / per_rank, rem = slot - r * per_rank;
+    const int u = x + n_xcd * (rem / G);
+    const int b = u / heads_kv, h = (u - b * heads_kv) * G + rem % G;
+    p.items[pos] = (uint32_t)(((int64_t)b * p.heads + h) * p.n_tiles + order[r]);
+  }
+}
+
 __device__ __forceinline__ void plan_items(const PlanParams& p) {
   __shared__ int bucket[NBUCKET];
   __shared__ int wave_sums[THREADS / 64];
   __shared__ uint16_t cached[MAX_CACHED];
   __shared__ PlanShared sh;
+  if (closed_form_plan(p)) {
+    plan_closed_form(p, (uint8_t*)cached, sh.unit_cost, bucket);
+    return;
+  }
   const bool cache = p.n_items <= MAX_CACHED;
   // A block layout shared by every (batch, head): the cost of a tile is the number of kept
   // columns (rows) in the union of its layout rows (columns), the same for every (batch, head).
