@@ -19,6 +19,7 @@ written before each one, so that the inputs come from HBM) and `gfx_clock` (the 
 amdsmi reports while the step runs, giving `pct_of_clock_adjusted_bf16_peak`).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--all]
+       python bench.py --fwd-only N | --bwd-only N [--steps K] [--warmup W]   (one workload, for traces)
 """
 
 from __future__ import annotations
@@ -596,6 +597,34 @@ def forward_only(cfg: int, calls: int, warmup: int) -> dict:
             "fwd_tflops": round(fl / med / 1e9, 2), "pct_peak": round(100 * fl / med / 1e9 / PEAK_BF16_TFLOPS, 2)}
 
 
+def backward_only(cfg: int, calls: int, warmup: int) -> dict:
+    """Backward of one bf16 workload only (two-pass default; O and LSE from one forward, dO from the
+    workload's seed), timed like forward_only; TFLOP/s counts 10*D flops per visible pair."""
+    import torch
+
+    from attention_attn_fwd_09_amd import binding as lib
+    from attention_attn_fwd_09_amd.inputs import WORKLOADS, workload_inputs
+
+    w = WORKLOADS[cfg]
+    if w.dtype != "bf16":
+        raise SystemExit(f"--bwd-only takes a bf16 workload (2-5), not {cfg}")
+    dev = torch.device("cuda:0")
+    inp = workload_inputs(cfg, with_do=True)
+    q, k, v, do = (inp[x].to(dev).contiguous() for x in ("q", "k", "v", "do"))
+    m = lib.Mask(kind=w.mask, lengths=None if inp["lengths"] is None else inp["lengths"].to(dev),
+                 layout=None if inp["layout"] is None else inp["layout"].to(dev))
+    o, lse = lib.attn_fwd(q, k, v, mask=m, scale=inp["scale"])
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(max(1, lib.attn_bwd_workspace_bytes(q, k, m)), dtype=torch.uint8, device=dev)
+    med, mn, mean = time_calls(torch, lambda: lib.attn_bwd(q, k, v, o, do, lse, mask=m, scale=inp["scale"], dq=dq,
+                                                             dk=dk, dv=dv, workspace=ws), n=calls, warm=warmup)
+    pairs = visible_pairs(w, inp)
+    fl = 10 * w.head_dim * pairs
+    return {"workload": w.name, "calls": calls, "bwd_ms": round(med, 5), "bwd_ms_min": round(mn, 5),
+            "bwd_ms_mean": round(mean, 5), "visible_pairs": pairs, "flops_per_call": fl,
+            "bwd_tflops": round(fl / med / 1e9, 2), "pct_peak": round(100 * fl / med / 1e9 / PEAK_BF16_TFLOPS, 2)}
+
+
 def fp8_diag(lib, torch, dev, workloads, workload_inputs):
     """Forward with fp8 (e4m3) inputs at the causal GQA workload's shape, against the same values
     in bf16; TFLOP/s counts 4*D flops per visible pair; the fp8 line is also given against the
@@ -727,6 +756,8 @@ def main():
     ap.add_argument("--fwd-only", type=int, default=0, metavar="CONFIG",
                     help="diagnostic: time only the forward of workload CONFIG (2-5) for --steps calls after "
                          "--warmup calls, print one JSON line and exit (for per-workload kernel traces)")
+    ap.add_argument("--bwd-only", type=int, default=0, metavar="CONFIG",
+                    help="diagnostic: likewise for the backward of workload CONFIG (2-5)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the attention path here is built and "
@@ -734,6 +765,9 @@ def main():
         sys.exit(2)
     if args.fwd_only:
         print(json.dumps(forward_only(args.fwd_only, args.steps, args.warmup)), flush=True)
+        return
+    if args.bwd_only:
+        print(json.dumps(backward_only(args.bwd_only, args.steps, args.warmup)), flush=True)
         return
     res = run_gpu(args)
     print(json.dumps(res), flush=True)
