@@ -582,6 +582,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdParams p) {
 // No product is computed twice; P crosses once per step, as bf16 (4 KiB per pair).
 // A step is one 64-row query tile of one query head of the group: copy barrier, P-wave scores and
 // exponentials (dP-wave scores alongside), exchange barrier, then the two gradient products.
+constexpr int PAIR_LEAD = 4;   // k-steps of row-fragment reads in flight ahead of the score MFMAs
+
 template <int D>
 struct PairLds {
   static constexpr int TILE = BQ * D * 2;
@@ -786,21 +788,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MINW))) voi
     return r;
   };
   // the two 32-query blocks' accumulators seeded from `st`, then += rows(tile) x frag^T (two
-  // interleaved MFMA chains)
+  // interleaved MFMA chains). The row-fragment reads run PAIR_LEAD k-steps ahead of the MFMAs that
+  // consume them (order pinned with sched_group_barrier; masks 0x100 LDS read, 0x008 MFMA).
   auto scores = [&](const char* tile, const char* st, f32x16 (&a)[2]) __attribute__((always_inline)) {
     a[0] = stats16(st, 0);
     a[1] = stats16(st, 1);
+    bf16x8 x0[KS], x1[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 x0 = *(const bf16x8*)(tile + roff[ks]);
-      const bf16x8 x1 = *(const bf16x8*)(tile + roff[ks] + 32 * RB);
-      a[0] = mfma32(x0, frag[ks], a[0]);
-      a[1] = mfma32(x1, frag[ks], a[1]);
+      x0[ks] = *(const bf16x8*)(tile + roff[ks]);
+      x1[ks] = *(const bf16x8*)(tile + roff[ks] + 32 * RB);
     }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      a[0] = mfma32(x0[ks], frag[ks], a[0]);
+      a[1] = mfma32(x1[ks], frag[ks], a[1]);
+    }
+    constexpr int KL = PAIR_LEAD < KS ? PAIR_LEAD : KS;
+    __builtin_amdgcn_sched_group_barrier(0x100, 8 + 2 * KL, 0);   // the 8 seed reads, KL k-steps
+#pragma unroll
+    for (int ks = 0; ks < KS - KL; ++ks) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * KL, 0);
   };
-  // acc += A^T B over the 32 queries of block qb: A = this lane's bf16 operand of chunk hc, B =
-  // transposed fragments of `tile` (rows qb*32 + hh*16 + hc*8 + 0..7)
-  auto grads = [&](const char* tile, int qb, const bf16x8 (&a)[2]) __attribute__((always_inline)) {
+  // transposed fragments of `tile` for query block qb (rows qb*32 + hh*16 + hc*8 + 0..7): the B
+  // operands of acc += A^T B. The tile does not change during a step, so a wave issues these reads
+  // before it waits at an exchange barrier and the barrier's wait covers their latency.
+  auto load_t = [&](const char* tile, int qb, bf16x8 (&t)[2][DB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int hc = 0; hc < 2; ++hc) {
       const int rows = (qb * 32 + hc * 8) * RB;
@@ -808,9 +824,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MINW))) voi
       for (int db = 0; db < DB; ++db) {
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, tile + toff[db][0] + rows));
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, tile + toff[db][1] + rows));
-        acc[db] = mfma32(a[hc], __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)),
-                         acc[db]);
+        t[hc][db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
+    }
+  };
+  // acc += A^T B over the 32 queries of one block: A = this lane's bf16 operand of chunk hc
+  auto grads = [&](const bf16x8 (&a)[2], const bf16x8 (&t)[2][DB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int hc = 0; hc < 2; ++hc) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[db] = mfma32(a[hc], t[hc][db], acc[db]);
     }
   };
 
@@ -844,9 +867,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MINW))) voi
     // P crosses one 32-query block at a time (one barrier per block), so that the P wave's
     // exponentials of block 1 run under its own dV products of block 0 and the dP wave starts on
     // block 0 half a step earlier.
+    bf16x8 t0[2][DB], t1[2][DB];   // transposed fragments of the two query blocks
     if constexpr (ROLE == 0) {
       f32x16 sc[2];
-      if (active) scores(ql, ST == 0 ? s_st0 : s_st1, sc);
+      if (active) {
+        scores(ql, ST == 0 ? s_st0 : s_st1, sc);
+        load_t(dol, 0, t0);
+      }
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         bf16x8 pb[2];
@@ -869,11 +896,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MINW))) voi
           *(bf16x8*)(xp + qb * 2048 + 1024) = pb[1];
         }
         lds_barrier();   // P of block qb is in LDS for the dP wave
-        if (active) grads(dol, qb, pb);   // dV += P^T dO
+        if (active) {
+          if (qb == 0) {
+            load_t(dol, 1, t1);
+            grads(pb, t0);   // dV += P^T dO
+          } else {
+            grads(pb, t1);
+          }
+        }
       }
     } else {
       f32x16 dp[2];
-      if (active) scores(dol, ST == 0 ? d_st0 : d_st1, dp);   // dP - Delta
+      if (active) {
+        scores(dol, ST == 0 ? d_st0 : d_st1, dp);   // dP - Delta
+        load_t(ql, 0, t0);
+      }
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         lds_barrier();
@@ -887,7 +924,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MINW))) voi
             ds[8 + i] = (float)p1[i] * dp[qb][8 + i];
           }
           const bf16x8 dsb[2] = {pack_bf16x8(ds), pack_bf16x8(ds + 8)};
-          grads(ql, qb, dsb);   // dK += dS^T Q
+          if (qb == 0) {
+            load_t(ql, 1, t1);
+            grads(dsb, t0);   // dK += dS^T Q
+          } else {
+            grads(dsb, t1);
+          }
         }
       }
     }

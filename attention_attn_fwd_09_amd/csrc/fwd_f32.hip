@@ -155,6 +155,7 @@ __device__ __forceinline__ float wave_sum(float x) {
 template <int D, int MASK>
 __global__ __launch_bounds__(64 * ROW_WAVES) void fwd_f32_row_kernel(FwdParams p, int64_t rows) {
   constexpr int DPL = D / 64;   // output columns per lane
+  constexpr int VC = 64 / DPL;  // keys of V in registers at a time (64 values per lane)
   const int lane = threadIdx.x & 63;
   const int64_t r = (int64_t)blockIdx.x * ROW_WAVES + (threadIdx.x >> 6);
   if (r >= rows) return;   // wave-uniform; the kernel has no barriers
@@ -219,13 +220,24 @@ __global__ __launch_bounds__(64 * ROW_WAVES) void fwd_f32_row_kernel(FwdParams p
     m_run = m_new;
 #pragma unroll
     for (int e = 0; e < DPL; ++e) acc[e] *= alpha;
+    // P V over the step's keys, VC keys at a time: the chunk's V values are all loaded before the
+    // first is used, so the loads of a chunk overlap instead of running one key after another
+    // (keys past the sequence read as 0; their P is 0)
     const int nj = min(64, p.seq_k - k0);   // keys of the step that exist
-#pragma unroll 8
-    for (int j = 0; j < nj; ++j) {
-      const float pb = __shfl(pj, j, 64);
-      const float* vrow = vg + (size_t)(k0 + j) * D;
+    for (int j0 = 0; j0 < nj; j0 += VC) {
+      float vv[VC][DPL];
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[e] = fmaf(pb, vrow[lane + 64 * e], acc[e]);
+      for (int j = 0; j < VC; ++j) {
+        const float* vrow = vg + (size_t)(k0 + j0 + j) * D;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) vv[j][e] = (j0 + j < nj) ? vrow[lane + 64 * e] : 0.0f;
+      }
+#pragma unroll
+      for (int j = 0; j < VC; ++j) {
+        const float pb = __shfl(pj, j0 + j, 64);
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) acc[e] = fmaf(pb, vv[j][e], acc[e]);
+      }
     }
   }
 
