@@ -583,6 +583,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdParams p) {
 // A step is one 64-row query tile of one query head of the group: copy barrier, P-wave scores and
 // exponentials (dP-wave scores alongside), exchange barrier, then the two gradient products.
 constexpr int PAIR_LEAD = 4;   // k-steps of row-fragment reads in flight ahead of the score MFMAs
+constexpr int PAIR_PRIO_MIN_STEPS = 24;   // steps per item from which the P wave runs at raised priority
 
 template <int D>
 struct PairLds {
@@ -869,6 +870,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MINW))) voi
     // block 0 half a step earlier.
     bf16x8 t0[2][DB], t1[2][DB];   // transposed fragments of the two query blocks
     if constexpr (ROLE == 0) {
+      // the P wave's scores and exponentials gate its partner: on long items they go first at the
+      // instruction arbiter (on items of a few steps this measured slower, so they do not)
+      if (n_steps >= PAIR_PRIO_MIN_STEPS) __builtin_amdgcn_s_setprio(2);
       f32x16 sc[2];
       if (active) {
         scores(ql, ST == 0 ? s_st0 : s_st1, sc);
@@ -895,6 +899,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MINW))) voi
           *(bf16x8*)(xp + qb * 2048) = pb[0];
           *(bf16x8*)(xp + qb * 2048 + 1024) = pb[1];
         }
+        if (qb == 1) __builtin_amdgcn_s_setprio(0);
         lds_barrier();   // P of block qb is in LDS for the dP wave
         if (active) {
           if (qb == 0) {
