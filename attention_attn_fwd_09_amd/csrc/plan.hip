@@ -158,7 +158,15 @@ __device__ __forceinline__ bool closed_form_plan(const PlanParams& p) {
 
 __device__ __forceinline__ void plan_closed_form(const PlanParams& p, uint8_t* lay, int* cost, int* order) {
   const int nbytes = p.nb_q * p.nb_k;
-  for (int i = threadIdx.x; i < nbytes; i += THREADS) lay[i] = p.layout[i];
+  if ((reinterpret_cast<uintptr_t>(p.layout) & 15) == 0) {
+    // 16 bytes per thread (the LDS copy is 16-byte aligned); the tail byte by byte
+    const int n16 = nbytes / 16;
+    for (int i = threadIdx.x; i < n16; i += THREADS)
+      reinterpret_cast<uint4*>(lay)[i] = reinterpret_cast<const uint4*>(p.layout)[i];
+    for (int i = n16 * 16 + threadIdx.x; i < nbytes; i += THREADS) lay[i] = p.layout[i];
+  } else {
+    for (int i = threadIdx.x; i < nbytes; i += THREADS) lay[i] = p.layout[i];
+  }
   for (int t = threadIdx.x; t < p.n_tiles; t += THREADS) cost[t] = 0;
   __syncthreads();
   // kept tiles in the union of each tile's layout rows (columns): one (tile, column) pair per thread
@@ -207,7 +215,7 @@ __device__ __forceinline__ void plan_closed_form(const PlanParams& p, uint8_t* l
 __device__ __forceinline__ void plan_items(const PlanParams& p) {
   __shared__ int bucket[NBUCKET];
   __shared__ int wave_sums[THREADS / 64];
-  __shared__ uint16_t cached[MAX_CACHED];
+  __shared__ __attribute__((aligned(16))) uint16_t cached[MAX_CACHED];
   __shared__ PlanShared sh;
   if (closed_form_plan(p)) {
     plan_closed_form(p, (uint8_t*)cached, sh.unit_cost, bucket);
