@@ -104,7 +104,7 @@ typedef struct {
  *               0 = skip the tile, non-zero = keep it. Strides of 0 share one
  *               layout across batch elements and/or heads. A tile on a ragged
  *               edge covers only the rows/columns that exist.
- *  block_q, block_k  BLOCK: tile sizes; this build supports 64 x 64.
+ *  block_q, block_k  BLOCK: tile sizes; the library supports 64 x 64.
  *  dense        DENSE: device uint8, one [seq_q][seq_k] row-major matrix per
  *               (b, h) at element offset b*dense_stride_b + h*dense_stride_h
  *               (h = query head); 0 = the score becomes -infinity, non-zero =
