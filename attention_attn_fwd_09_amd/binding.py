@@ -36,6 +36,7 @@ ATTN_BF16 = 1
 ATTN_FP8_E4M3 = 2  # forward inputs only; O is bf16
 
 ATTN_BWD_ATOMIC_DQ = 1  # attn_bwd_ex flag: single-pass backward with atomic fp32 dQ accumulation
+ATTN_BWD_PLANNED = 2    # attn_bwd_ex flag: the workspace holds lists written by attn_fwd_with_bwd_plan
 
 MASK_KINDS = {"none": 0, "causal": 1, "padding": 2, "block": 3, "dense": 4}
 
@@ -98,6 +99,8 @@ def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
     lib.attn_bwd_ex.restype = ctypes.c_int
     lib.attn_bwd_ex_workspace_bytes.argtypes = [pp, pm, ctypes.c_int32]
     lib.attn_bwd_ex_workspace_bytes.restype = sz
+    lib.attn_fwd_with_bwd_plan.argtypes = [pp, vp, vp, vp, pm, ctypes.c_float, vp, vp, vp, sz, vp, sz, vp]
+    lib.attn_fwd_with_bwd_plan.restype = ctypes.c_int
     lib.attn_bwd_noalloc.argtypes = [pp, vp, vp, vp, vp, vp, vp, pm, ctypes.c_float, vp, vp, vp, vp]
     lib.attn_bwd_noalloc.restype = ctypes.c_int
     lib.attn_bwd_noalloc_scratch_bytes.argtypes = []
@@ -291,16 +294,23 @@ def _on_stream(stream):
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Optional[Mask] = None,
              scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
              lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None,
-             kv_splits: int = 0):
+             kv_splits: int = 0, bwd_plan: Optional[torch.Tensor] = None):
     """Forward: returns (O, LSE). O has q's dtype (bf16 for fp8 inputs); LSE is float32
     [batch, heads_q, seq_q].
 
     kv_splits: 0 lets the library choose a split of each item's key range, 1 never splits,
-    n > 1 forces n splits (attn_fwd_ex). Every tensor is checked against the layout of
-    include/attn.h before the call; the library itself checks sizes, alignment and overlaps."""
+    n > 1 forces n splits (attn_fwd_ex). bwd_plan: a backward workspace (uint8 tensor of
+    attn_bwd_workspace_bytes bytes) into which the same planner launch also writes the backward's
+    work lists (attn_fwd_with_bwd_plan; kv_splits must then be 0); pass it to attn_bwd with
+    planned=True. Every tensor is checked against the layout of include/attn.h before the call;
+    the library itself checks sizes, alignment and overlaps."""
     lib = load_library()
     mask = mask or Mask()
     prob = _check_inputs(q, k, v, mask)
+    if bwd_plan is not None:
+        if kv_splits != 0:
+            raise ValueError("bwd_plan takes the library's own key-range split (kv_splits=0)")
+        _check_workspace(bwd_plan, q.device)
     o_dtype = torch.bfloat16 if q.dtype == torch.float8_e4m3fn else q.dtype
     if out is not None:
         _expect(out, "out", q.shape, o_dtype, q.device)
@@ -321,9 +331,15 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Optional[M
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = lib.attn_fwd_ex(ctypes.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(cm),
-                         float(scale), out.data_ptr(), lse.data_ptr(), ws_ptr, ws_bytes, int(kv_splits),
-                         _stream_ptr(stream))
+    if bwd_plan is not None:
+        st = lib.attn_fwd_with_bwd_plan(ctypes.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                        ctypes.byref(cm), float(scale), out.data_ptr(), lse.data_ptr(), ws_ptr,
+                                        ws_bytes, bwd_plan.data_ptr(), bwd_plan.numel() * bwd_plan.element_size(),
+                                        _stream_ptr(stream))
+    else:
+        st = lib.attn_fwd_ex(ctypes.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(cm),
+                             float(scale), out.data_ptr(), lse.data_ptr(), ws_ptr, ws_bytes, int(kv_splits),
+                             _stream_ptr(stream))
     _raise(st)
     return out, lse
 
@@ -332,15 +348,21 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
              lse: torch.Tensor, mask: Optional[Mask] = None, scale: Optional[float] = None,
              dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
              dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None,
-             flags: int = 0):
+             flags: int = 0, planned: bool = False):
     """Backward: returns (dQ, dK, dV) in q's dtype.
 
     flags: 0 (two passes, deterministic) or ATTN_BWD_ATOMIC_DQ (single pass, dQ accumulated with
-    fp32 atomics; attn_bwd_ex). o and do have q's shape and dtype, lse is float32
-    [batch, heads_q, seq_q]; dq, dk, dv (when given) have the shapes of q, k, v."""
+    fp32 atomics; attn_bwd_ex). planned: `workspace` already holds the work lists that
+    attn_fwd(..., bwd_plan=workspace) wrote for the same problem and mask (ATTN_BWD_PLANNED; no
+    planner launch). o and do have q's shape and dtype, lse is float32 [batch, heads_q, seq_q];
+    dq, dk, dv (when given) have the shapes of q, k, v."""
     lib = load_library()
     mask = mask or Mask()
     prob = _check_inputs(q, k, v, mask)
+    if planned:
+        if workspace is None:
+            raise ValueError("planned=True needs the workspace attn_fwd(..., bwd_plan=...) planned into")
+        flags = int(flags) | ATTN_BWD_PLANNED
     _expect(o, "o", q.shape, q.dtype, q.device)
     _expect(do, "do", q.shape, q.dtype, q.device)
     _expect(lse, "lse", q.shape[:3], torch.float32, q.device)

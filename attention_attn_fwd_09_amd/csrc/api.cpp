@@ -273,6 +273,45 @@ BwdSizes bwd_sizes(const attn_problem* p, const attn_mask* m, int32_t flags = 0)
   return s;
 }
 
+// Problems the backward supports beyond check_problem: bf16, and for block and dense masks at most
+// bwd_max_steps() listed (query head, layout row) pairs per key column (6 + 10 bits each).
+attn_status check_bwd_support(const attn_problem* p, const attn_mask* m) {
+  if (p->dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (m->kind == ATTN_MASK_BLOCK || m->kind == ATTN_MASK_DENSE) {
+    const int64_t nbq = ceil_div(p->seq_q, 64), group = p->heads_q / p->heads_kv;
+    if (nbq > 1024 || group > 63 || group * nbq > bwd_max_steps()) return ATTN_ERR_UNSUPPORTED;
+  }
+  return ATTN_OK;
+}
+
+// The bytes of the caller's mask data (lengths, layout or dense mask; empty for none and causal).
+Range mask_data_range(const attn_problem* p, const attn_mask* m) {
+  if (m->kind == ATTN_MASK_PADDING) return range_of(m->lengths, (size_t)p->batch * 4);
+  if (m->kind == ATTN_MASK_BLOCK) return range_of(m->block_layout, (size_t)layout_bytes(p, m));
+  if (m->kind == ATTN_MASK_DENSE) return range_of(m->dense, (size_t)dense_bytes(p, m));
+  return Range{0, 0};
+}
+
+// Planner parameters of the backward's two lists (into workspace `ws` laid out by bs), on a block
+// layout (the caller's, or one derived from a dense mask) with these strides.
+void bwd_plan_params(const attn_problem* p, const attn_mask* m, const BwdSizes& bs, const uint8_t* layout,
+                     int64_t layout_stride_b, int64_t layout_stride_h, char* ws, PlanParams* pk, PlanParams* pq) {
+  PlanParams pp;
+  std::memset(&pp, 0, sizeof(pp));
+  pp.mask = m->kind == ATTN_MASK_DENSE ? ATTN_MASK_BLOCK : m->kind;
+  pp.group = p->heads_q / p->heads_kv; pp.seq_q = p->seq_q; pp.seq_k = p->seq_k;
+  pp.nb_q = ceil_div(p->seq_q, 64); pp.nb_k = ceil_div(p->seq_k, 64);
+  pp.lengths = m->lengths; pp.layout = layout;
+  pp.layout_stride_b = layout_stride_b; pp.layout_stride_h = layout_stride_h;
+  pp.n_xcd = device_info().xcds;
+  *pk = pp;
+  *pq = pp;
+  pk->mode = PLAN_BWD_KV; pk->heads = p->heads_kv; pk->n_tiles = bs.n_kt; pk->tile = bs.bk;
+  pk->n_items = (int32_t)bs.kv_items; pk->items = (uint32_t*)(ws + bs.kv_off);
+  pq->mode = PLAN_FWD_Q; pq->heads = p->heads_q; pq->n_tiles = bs.n_qt; pq->tile = bs.bq;
+  pq->n_items = (int32_t)bs.q_items; pq->items = (uint32_t*)(ws + bs.q_off);
+}
+
 attn_status hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
 
 // Optional per-class event brackets (attn_set_timing_events).
@@ -369,8 +408,29 @@ attn_status attn_fwd(const attn_problem* problem, const void* Q, const void* K, 
 attn_status attn_fwd_ex(const attn_problem* problem, const void* Q, const void* K, const void* V,
                         const attn_mask* mask, float scale, void* O, float* LSE, void* workspace,
                         size_t workspace_bytes, int32_t kv_splits, void* stream) {
+  return attn::fwd_call(problem, Q, K, V, mask, scale, O, LSE, workspace, workspace_bytes, kv_splits, nullptr, 0,
+                        false, stream);
+}
+
+attn_status attn_fwd_with_bwd_plan(const attn_problem* problem, const void* Q, const void* K, const void* V,
+                                   const attn_mask* mask, float scale, void* O, float* LSE, void* workspace,
+                                   size_t workspace_bytes, void* bwd_workspace, size_t bwd_workspace_bytes,
+                                   void* stream) {
+  return attn::fwd_call(problem, Q, K, V, mask, scale, O, LSE, workspace, workspace_bytes, 0, bwd_workspace,
+                        bwd_workspace_bytes, true, stream);
+}
+
+}  // extern "C"
+
+namespace attn {
+
+attn_status fwd_call(const attn_problem* problem, const void* Q, const void* K, const void* V,
+                     const attn_mask* mask, float scale, void* O, float* LSE, void* workspace,
+                     size_t workspace_bytes, int32_t kv_splits, void* bwd_workspace, size_t bwd_workspace_bytes,
+                     bool plan_bwd, void* stream) {
   if (problem == nullptr || Q == nullptr || K == nullptr || V == nullptr || O == nullptr || LSE == nullptr)
     return ATTN_ERR_NULL;
+  if (plan_bwd && bwd_workspace == nullptr) return ATTN_ERR_NULL;
   const attn_mask* m = mask ? mask : &kNoMask;
   const attn_problem* p = problem;
   attn_status st = check_problem(p, m, scale);
@@ -410,6 +470,21 @@ attn_status attn_fwd_ex(const attn_problem* problem, const void* Q, const void* 
   if (m->kind == ATTN_MASK_DENSE) {
     const Range rden = range_of(m->dense, (size_t)dense_bytes(p, m));
     if (overlap(rden, ro) || overlap(rden, rl) || (need > 0 && overlap(rden, rw))) return ATTN_ERR_ALIAS;
+  }
+  // the backward's lists: a problem the backward supports, and a workspace of its size that
+  // overlaps nothing else of the call
+  BwdSizes bs{};
+  if (plan_bwd) {
+    st = check_bwd_support(p, m);
+    if (st != ATTN_OK) return st;
+    bs = bwd_sizes(p, m, 0);
+    if (bwd_workspace_bytes < bs.total) return ATTN_ERR_WORKSPACE;
+    if (!aligned16(bwd_workspace)) return ATTN_ERR_ALIGN;
+    const Range rb = range_of(bwd_workspace, bs.total);
+    for (Range r : {rq, rk, rv, ro, rl})
+      if (overlap(rb, r)) return ATTN_ERR_ALIAS;
+    if (need > 0 && overlap(rb, rw)) return ATTN_ERR_ALIAS;
+    if (overlap(rb, mask_data_range(p, m))) return ATTN_ERR_ALIAS;
   }
 
   // ---- launch ----
@@ -454,6 +529,10 @@ attn_status attn_fwd_ex(const attn_problem* problem, const void* Q, const void* 
     }));
     if (st != ATTN_OK) return st;
   }
+  // the backward's two lists, planned on the same layout the forward plans on
+  PlanParams pk, pq;
+  if (plan_bwd)
+    bwd_plan_params(p, m, bs, fp.layout, fp.layout_stride_b, fp.layout_stride_h, (char*)bwd_workspace, &pk, &pq);
   if (fz.plan_bytes > 0) {
     PlanParams pp;
     std::memset(&pp, 0, sizeof(pp));
@@ -465,9 +544,15 @@ attn_status attn_fwd_ex(const attn_problem* problem, const void* Q, const void* 
     pp.layout_stride_b = fp.layout_stride_b; pp.layout_stride_h = fp.layout_stride_h;
     pp.items = (uint32_t*)workspace;
     pp.n_xcd = fp.n_xcd;
-    st = hip_status(timed(ATTN_KERNEL_PLAN, s, [&] { return launch_plan(pp, s); }));
+    st = hip_status(timed(ATTN_KERNEL_PLAN, s, [&] {
+      return plan_bwd ? launch_plan_triple(pp, pk, pq, s) : launch_plan(pp, s);
+    }));
     if (st != ATTN_OK) return st;
     fp.items = (const uint32_t*)workspace;
+  } else if (plan_bwd) {
+    // the forward orders its items in closed form; the backward's lists still need a launch
+    st = hip_status(timed(ATTN_KERNEL_PLAN, s, [&] { return launch_plan_pair(pk, pq, s); }));
+    if (st != ATTN_OK) return st;
   }
   if (p->dtype == ATTN_FP8_E4M3)
     st = hip_status(timed(ATTN_KERNEL_FWD, s, [&] { return launch_fwd_fp8(fp, p->head_dim, m->kind, s); }));
@@ -477,12 +562,17 @@ attn_status attn_fwd_ex(const attn_problem* problem, const void* Q, const void* 
   return hip_status(timed(ATTN_KERNEL_FWD_MERGE, s, [&] { return launch_fwd_merge(fp, p->head_dim, s); }));
 }
 
+}  // namespace attn
+
+extern "C" {
+
 size_t attn_bwd_ex_workspace_bytes(const attn_problem* problem, const attn_mask* mask, int32_t flags) {
   if (problem == nullptr) return 0;
   const attn_mask* m = mask ? mask : &kNoMask;
   if (check_problem(problem, m, 1.0f) != ATTN_OK) return 0;
-  if (problem->dtype != ATTN_BF16 || (flags & ~ATTN_BWD_ATOMIC_DQ) != 0) return 0;
-  return bwd_sizes(problem, m, flags).total;
+  if (problem->dtype != ATTN_BF16 || (flags & ~(ATTN_BWD_ATOMIC_DQ | ATTN_BWD_PLANNED)) != 0) return 0;
+  if ((flags & ATTN_BWD_ATOMIC_DQ) && (flags & ATTN_BWD_PLANNED)) return 0;
+  return bwd_sizes(problem, m, flags & ATTN_BWD_ATOMIC_DQ).total;
 }
 
 size_t attn_bwd_workspace_bytes(const attn_problem* problem, const attn_mask* mask) {
@@ -517,17 +607,15 @@ attn_status bwd_call(const attn_problem* problem, const void* Q, const void* K, 
   const attn_problem* p = problem;
   attn_status st = check_problem(p, m, scale);
   if (st != ATTN_OK) return st;
-  if ((flags & ~ATTN_BWD_ATOMIC_DQ) != 0) return ATTN_ERR_SHAPE;
+  if ((flags & ~(ATTN_BWD_ATOMIC_DQ | ATTN_BWD_PLANNED)) != 0) return ATTN_ERR_SHAPE;
   const bool atomic_dq = (flags & ATTN_BWD_ATOMIC_DQ) != 0;
-  if (p->dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
-  if (m->kind == ATTN_MASK_BLOCK || m->kind == ATTN_MASK_DENSE) {
-    // the dK/dV pass lists (query head, layout row) pairs of its column: 6 + 10 bits each
-    const int64_t nbq = ceil_div(p->seq_q, 64), group = p->heads_q / p->heads_kv;
-    if (nbq > 1024 || group > 63 || group * nbq > bwd_max_steps()) return ATTN_ERR_UNSUPPORTED;
-  }
+  const bool planned = (flags & ATTN_BWD_PLANNED) != 0;
+  if (atomic_dq && planned) return ATTN_ERR_UNSUPPORTED;
+  st = check_bwd_support(p, m);
+  if (st != ATTN_OK) return st;
   for (const void* ptr : {Q, K, V, O, dO, (const void*)LSE, (const void*)dQ, (const void*)dK, (const void*)dV})
     if (!aligned16(ptr)) return ATTN_ERR_ALIGN;
-  const BwdSizes bs = bwd_sizes(p, m, flags);
+  const BwdSizes bs = bwd_sizes(p, m, flags & ATTN_BWD_ATOMIC_DQ);
 
   const size_t es = 2;
   const size_t qbytes = (size_t)p->batch * p->heads_q * p->seq_q * p->head_dim * es;
@@ -593,22 +681,13 @@ attn_status bwd_call(const attn_problem* problem, const void* Q, const void* K, 
     if (st != ATTN_OK) return st;
   }
 
-  PlanParams pp;
-  std::memset(&pp, 0, sizeof(pp));
-  pp.mask = m->kind == ATTN_MASK_DENSE ? ATTN_MASK_BLOCK : m->kind;
-  pp.group = bp.group; pp.seq_q = p->seq_q; pp.seq_k = p->seq_k;
-  pp.nb_q = bp.nb_q; pp.nb_k = bp.nb_k; pp.lengths = m->lengths; pp.layout = bp.layout;
-  pp.layout_stride_b = bp.layout_stride_b; pp.layout_stride_h = bp.layout_stride_h;
-  pp.n_xcd = device_info().xcds;
-  // dK/dV items (b, kv head, key tile) and dQ items (b, query head, query tile), one launch
-  PlanParams pk = pp, pq = pp;
-  pk.mode = PLAN_BWD_KV; pk.heads = p->heads_kv; pk.n_tiles = bs.n_kt; pk.tile = bs.bk;
-  pk.n_items = (int32_t)bs.kv_items; pk.items = (uint32_t*)(ws + bs.kv_off);
-  pq.mode = PLAN_FWD_Q; pq.heads = p->heads_q; pq.n_tiles = bs.n_qt; pq.tile = bs.bq;
-  pq.n_items = (int32_t)bs.q_items; pq.items = (uint32_t*)(ws + bs.q_off);
+  // dK/dV items (b, kv head, key tile) and dQ items (b, query head, query tile), one launch (none
+  // when the forward of the pair already wrote them into this workspace)
+  PlanParams pk, pq;
+  bwd_plan_params(p, m, bs, bp.layout, bp.layout_stride_b, bp.layout_stride_h, ws, &pk, &pq);
   if (atomic_dq)
     st = hip_status(timed(ATTN_KERNEL_PLAN, s, [&] { return launch_plan(pk, s); }));
-  else
+  else if (!planned)
     st = hip_status(timed(ATTN_KERNEL_PLAN, s, [&] { return launch_plan_pair(pk, pq, s); }));
   if (st != ATTN_OK) return st;
 

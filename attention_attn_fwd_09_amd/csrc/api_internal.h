@@ -1,4 +1,4 @@
-// Internal entry shared by the backward entry points of the C ABI (no device code here).
+// Internal entries shared by the entry points of the C ABI (no device code here).
 #pragma once
 
 #include <stddef.h>
@@ -17,5 +17,12 @@ attn_status bwd_call(const attn_problem* problem, const void* Q, const void* K, 
                      const void* dO, const float* LSE, const attn_mask* mask, float scale, void* dQ, void* dK,
                      void* dV, void* workspace, size_t workspace_bytes, int32_t flags, void* stream,
                      WorkspaceProvider provide);
+
+// attn_fwd_ex (plan_bwd false) and attn_fwd_with_bwd_plan (plan_bwd true: one planner launch also
+// writes the backward's two lists into bwd_workspace).
+attn_status fwd_call(const attn_problem* problem, const void* Q, const void* K, const void* V,
+                     const attn_mask* mask, float scale, void* O, float* LSE, void* workspace,
+                     size_t workspace_bytes, int32_t kv_splits, void* bwd_workspace, size_t bwd_workspace_bytes,
+                     bool plan_bwd, void* stream);
 
 }  // namespace attn

@@ -26,6 +26,7 @@
 // contraction dimension of a row-major tile come from LDS through ds_read_b64_tr_b16.
 #include <type_traits>
 
+#include "attn.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -122,6 +123,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdParams p) {
   const int dsub = ((lane >> 4) & 1) * 16, i16 = lane & 15;
 
   const uint32_t item = p.items_kv[blockIdx.x];
+  // an item outside the problem (a list the caller kept from another call) does nothing
+  if ((uint64_t)item >= (uint64_t)p.batch * p.heads_kv * p.n_ktiles) return;
   const int kt = (int)(item % (uint32_t)p.n_ktiles);
   const int bkv = (int)(item / (uint32_t)p.n_ktiles);
   const int kvh = bkv % p.heads_kv, b = bkv / p.heads_kv;
@@ -641,6 +644,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MINW))) voi
   const int pair = rank >> 1, role = (rank & 1) ^ slot;   // role 0: S, P, dV; role 1: dP, dS, dK
 
   const uint32_t item = p.items_kv[blockIdx.x];
+  // an item outside the problem (a list the caller kept from another call) does nothing
+  if ((uint64_t)item >= (uint64_t)p.batch * p.heads_kv * p.n_ktiles) return;
   const int kt = (int)(item % (uint32_t)p.n_ktiles);
   const int bkv = (int)(item / (uint32_t)p.n_ktiles);
   const int kvh = bkv % p.heads_kv, b = bkv / p.heads_kv;
@@ -1002,7 +1007,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
   const int c = lane & 31, hh = lane >> 5;
   const int dsub = ((lane >> 4) & 1) * 16, i16 = lane & 15;
 
-  const Item it = decode_item(p.items_q[blockIdx.x], p.heads_q, p.n_qtiles);
+  const uint32_t item = p.items_q[blockIdx.x];
+  // an item outside the problem (a list the caller kept from another call) does nothing
+  if ((uint64_t)item >= (uint64_t)p.batch * p.heads_q * p.n_qtiles) return;
+  const Item it = decode_item(item, p.heads_q, p.n_qtiles);
   const int b = it.b, h = it.h, kvh = h / p.group;
   const int q0 = it.t * BM;
   const int qw0 = q0 + wave * 32;
@@ -1343,7 +1351,7 @@ hipError_t dq_mask(const BwdParams& p, int mask, int n_items, hipStream_t s) {
 // keys, or one 64-key layout column for block masks (2 waves).
 int bwd_block_q(int head_dim, int mask) { (void)head_dim; (void)mask; return 128; }
 int bwd_dkdv_variant(int mask, int flags, int group, int nb_q) {
-  if (flags != 0) return DKDV_ONE_WAVE;
+  if ((flags & ATTN_BWD_ATOMIC_DQ) != 0) return DKDV_ONE_WAVE;
   if ((mask == MASK_BLOCK || mask == MASK_DENSE) && (int64_t)group * nb_q > PairLds<128>::MAX_STEPS)
     return DKDV_ONE_WAVE;
   return DKDV_PAIR;

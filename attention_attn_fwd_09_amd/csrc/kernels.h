@@ -46,6 +46,7 @@ hipError_t launch_dense_pack(const DensePackParams& p, hipStream_t stream);
 
 hipError_t launch_plan(const PlanParams& p, hipStream_t stream);
 hipError_t launch_plan_pair(const PlanParams& a, const PlanParams& b, hipStream_t stream);
+hipError_t launch_plan_triple(const PlanParams& a, const PlanParams& b, const PlanParams& c, hipStream_t stream);
 
 int fwd_bf16_block_m(int head_dim, int mask);
 hipError_t launch_fwd_bf16(const FwdParams& p, int head_dim, int mask, hipStream_t stream);

@@ -302,6 +302,12 @@ __global__ __launch_bounds__(THREADS) void plan_pair_kernel(PlanParams a, PlanPa
   plan_items(blockIdx.x == 0 ? a : b);
 }
 
+// Three lists in one launch: the forward's and the backward's two, when a forward also plans the
+// backward that follows it.
+__global__ __launch_bounds__(THREADS) void plan_triple_kernel(PlanParams a, PlanParams b, PlanParams c) {
+  plan_items(blockIdx.x == 0 ? a : (blockIdx.x == 1 ? b : c));
+}
+
 }  // namespace
 
 hipError_t launch_plan(const PlanParams& p, hipStream_t stream) {
@@ -311,6 +317,11 @@ hipError_t launch_plan(const PlanParams& p, hipStream_t stream) {
 
 hipError_t launch_plan_pair(const PlanParams& a, const PlanParams& b, hipStream_t stream) {
   hipLaunchKernelGGL(plan_pair_kernel, dim3(2), dim3(THREADS), 0, stream, a, b);
+  return hipGetLastError();
+}
+
+hipError_t launch_plan_triple(const PlanParams& a, const PlanParams& b, const PlanParams& c, hipStream_t stream) {
+  hipLaunchKernelGGL(plan_triple_kernel, dim3(3), dim3(THREADS), 0, stream, a, b, c);
   return hipGetLastError();
 }
 

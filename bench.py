@@ -2,7 +2,8 @@
 """Benchmark of the attention hot path on one MI355X.
 
 A step is one pass of the whole hot path over one batch of synthetic input: the fused forward
-(O, LSE) and the backward (dQ, dK, dV) of the block-sparse workload (batch 2, 16 heads, seq 4096,
+(O, LSE; its one planner launch also plans the backward) and the backward (dQ, dK, dV) of the
+block-sparse workload (batch 2, 16 heads, seq 4096,
 head_dim 128, 64x64 blocks kept with p = 0.25 plus the diagonal), the only measured workload that
 exercises every step of the path. Inputs are resident in HBM before the timed region starts.
 Before the W warm-up steps, 0.25 s of untimed steps bring the graphics clock to its steady state
@@ -273,10 +274,12 @@ def run_gpu(args):
     ws_b = torch.empty(max(1, lib.attn_bwd_workspace_bytes(q, k, mask)), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
+    # the forward's planner launch also writes the backward's two lists into the backward's
+    # workspace (attn_fwd_with_bwd_plan), and the backward then launches no planner of its own
     def step():
-        lib.attn_fwd(q, k, v, mask=mask, scale=scale, out=o, lse=lse, workspace=ws_f, stream=stream)
+        lib.attn_fwd(q, k, v, mask=mask, scale=scale, out=o, lse=lse, workspace=ws_f, stream=stream, bwd_plan=ws_b)
         lib.attn_bwd(q, k, v, o, do, lse, mask=mask, scale=scale, dq=dq, dk=dk, dv=dv, workspace=ws_b,
-                     stream=stream)
+                     stream=stream, planned=True)
 
     pairs = visible_pairs(w, inp)
     d = w.head_dim
@@ -388,7 +391,7 @@ def run_gpu(args):
             "workload": w.name,
             "batch": w.batch, "heads": w.heads_q, "seq_len": w.seq_q, "head_dim": d,
             "mask": "block 64x64, p=0.25 + diagonal (shared by all heads)",
-            "step": "attn_fwd + attn_bwd",
+            "step": "attn_fwd (its planner launch also plans the backward) + attn_bwd (planned)",
             "visible_pairs": pairs,
             "flops_per_step": flops_step,
             "fwd_tflops_share": round(flops_fwd / flops_step, 4),

@@ -193,12 +193,19 @@ enum {
    * workspace with hardware float atomics, and a convert kernel writes dQ = scale * accumulator
    * in bf16: no second recomputation of S and dP, but dQ depends on the order of the atomic
    * additions (not bitwise reproducible from run to run; dK and dV still are). */
-  ATTN_BWD_ATOMIC_DQ = 1
+  ATTN_BWD_ATOMIC_DQ = 1,
+  /* The workspace already holds the backward's two work lists, written by
+   * attn_fwd_with_bwd_plan (below) for the same problem and mask, with the mask's data unchanged
+   * since and no other use of the workspace in between: the call launches no planner. The
+   * library cannot check the lists' contents; a list from another problem only makes its
+   * out-of-range items do nothing (wrong results, no out-of-bounds access). Not combinable with
+   * ATTN_BWD_ATOMIC_DQ (ATTN_ERR_UNSUPPORTED). */
+  ATTN_BWD_PLANNED = 2
 };
 
 /*
- * Backward with options (flags: 0 or ATTN_BWD_ATOMIC_DQ). Arguments, outputs and errors as for
- * attn_bwd; an unknown flag returns ATTN_ERR_SHAPE; the workspace must hold
+ * Backward with options (flags: 0, ATTN_BWD_ATOMIC_DQ or ATTN_BWD_PLANNED). Arguments, outputs
+ * and errors as for attn_bwd; an unknown flag returns ATTN_ERR_SHAPE; the workspace must hold
  * attn_bwd_ex_workspace_bytes(problem, mask, flags) bytes (with ATTN_BWD_ATOMIC_DQ it includes
  * a float32 [batch, heads_q, seq_q, head_dim] accumulator).
  */
@@ -209,6 +216,26 @@ attn_status attn_bwd_ex(const attn_problem *problem, const void *Q, const void *
 
 /* Workspace bytes of attn_bwd_ex with these flags (0 for an invalid problem or flag). */
 size_t attn_bwd_ex_workspace_bytes(const attn_problem *problem, const attn_mask *mask, int32_t flags);
+
+/*
+ * Forward that also plans the backward which follows it. The report on the sparse FlashAttention
+ * operator (Xingchen-Cup, smzdm.com) opens with a slow statistics prologue that cost more than it
+ * saved, and its section 03 asks for the uneven sparse blocks to be spread evenly over the cores;
+ * the planner that orders the work items longest first is that spreading, and this entry point
+ * runs it once per forward/backward pair instead of once per call: one planner launch writes the
+ * forward's list into `workspace` and the backward's two lists into `bwd_workspace`. The forward
+ * is attn_fwd's (the library chooses the key-range split). A later attn_bwd_ex with
+ * ATTN_BWD_PLANNED on `bwd_workspace` then launches no planner.
+ * bwd_workspace: device memory of attn_bwd_workspace_bytes(problem, mask) bytes, 16-byte aligned,
+ *   owned by the caller, overlapping no input, output, mask or `workspace`.
+ * Errors: as attn_fwd, and ATTN_ERR_NULL (bwd_workspace null), ATTN_ERR_WORKSPACE (too small),
+ * ATTN_ERR_ALIGN, ATTN_ERR_ALIAS, ATTN_ERR_UNSUPPORTED (a problem attn_bwd does not support,
+ * such as an F32 or F8 dtype), all checked before any launch.
+ */
+attn_status attn_fwd_with_bwd_plan(const attn_problem *problem, const void *Q, const void *K, const void *V,
+                                   const attn_mask *mask, float scale, void *O, float *LSE, void *workspace,
+                                   size_t workspace_bytes, void *bwd_workspace, size_t bwd_workspace_bytes,
+                                   void *stream);
 
 /*
  * Backward that allocates nothing, for callers that cannot allocate device memory: code under HIP

@@ -253,16 +253,53 @@ def test_single_pass_backward_arguments():
     assert two == lib.attn_bwd_workspace_bytes(ctypes.byref(p), ctypes.byref(m))
     # the single pass keeps an fp32 [B, Hq, Sq, D] dQ accumulator instead of the dQ item list
     assert one >= 2 * 4 * 300 * 128 * 4
-    assert lib.attn_bwd_ex_workspace_bytes(ctypes.byref(p), ctypes.byref(m), 2) == 0
+    assert lib.attn_bwd_ex_workspace_bytes(ctypes.byref(p), ctypes.byref(m), 4) == 0
+    # the planned backward uses the two-pass layout; it does not combine with the single pass
+    assert lib.attn_bwd_ex_workspace_bytes(ctypes.byref(p), ctypes.byref(m), B.ATTN_BWD_PLANNED) == two
+    assert lib.attn_bwd_ex_workspace_bytes(ctypes.byref(p), ctypes.byref(m),
+                                           B.ATTN_BWD_PLANNED | B.ATTN_BWD_ATOMIC_DQ) == 0
 
     def call(flags, wsb):
         return lib.attn_bwd_ex(ctypes.byref(p), q, k, v, o, do, lse, ctypes.byref(m), 0.1, dq, dk, dv, ws, wsb,
                                flags, None)
 
-    assert call(2, 1 << 40) == B.ATTN_ERR_SHAPE
+    assert call(4, 1 << 40) == B.ATTN_ERR_SHAPE
     assert call(-1, 1 << 40) == B.ATTN_ERR_SHAPE
     assert call(B.ATTN_BWD_ATOMIC_DQ, one - 1) == B.ATTN_ERR_WORKSPACE
     assert call(B.ATTN_BWD_ATOMIC_DQ, two) == B.ATTN_ERR_WORKSPACE
+    assert call(B.ATTN_BWD_PLANNED | B.ATTN_BWD_ATOMIC_DQ, 1 << 40) == B.ATTN_ERR_UNSUPPORTED
+    assert call(B.ATTN_BWD_PLANNED, two - 1) == B.ATTN_ERR_WORKSPACE
+
+
+def _fwd_plan(lib, p, m, bws, bws_bytes, ptrs=None):
+    ptrs = ptrs or _fwd_ok_ptrs()
+    return lib.attn_fwd_with_bwd_plan(ctypes.byref(p), ptrs["q"], ptrs["k"], ptrs["v"], ctypes.byref(m), 0.125,
+                                      ptrs["o"], ptrs["lse"], ptrs["ws"], 1 << 40, bws, bws_bytes, None)
+
+
+def test_forward_with_backward_plan_arguments():
+    """Host-side rejections of attn_fwd_with_bwd_plan (nothing is launched)."""
+    lib = _lib()
+    p, m = _problem(b=2, hq=4, hkv=2, sq=300, sk=300, d=128), _mask()
+    need = lib.attn_bwd_workspace_bytes(ctypes.byref(p), ctypes.byref(m))
+    bws = _spaced(8)[7]
+    assert _fwd_plan(lib, p, m, None, need) == B.ATTN_ERR_NULL
+    assert _fwd_plan(lib, p, m, bws, need - 1) == B.ATTN_ERR_WORKSPACE
+    assert _fwd_plan(lib, p, m, bws + 8, need) == B.ATTN_ERR_ALIGN
+    ptrs = _fwd_ok_ptrs()
+    assert _fwd_plan(lib, p, m, ptrs["q"] + 256, need, ptrs) == B.ATTN_ERR_ALIAS      # inside Q
+    # a block mask: the forward has a workspace (its own list) and the layout is mask data
+    layout = _spaced(9)[8]
+    mb = _mask(kind=3, layout=layout)
+    need_b = lib.attn_bwd_workspace_bytes(ctypes.byref(p), ctypes.byref(mb))
+    assert _fwd_plan(lib, p, mb, ptrs["ws"], need_b, ptrs) == B.ATTN_ERR_ALIAS       # the forward's workspace
+    assert _fwd_plan(lib, p, mb, layout, need_b, ptrs) == B.ATTN_ERR_ALIAS           # the layout
+    # problems the backward does not support: F32 and FP8 inputs
+    for dtype in (B.ATTN_F32, B.ATTN_FP8_E4M3):
+        pf = _problem(b=2, hq=4, hkv=2, sq=300, sk=300, d=128, dtype=dtype)
+        assert _fwd_plan(lib, pf, m, bws, 1 << 40) == B.ATTN_ERR_UNSUPPORTED
+    # the forward's own checks still come first
+    assert _fwd_plan(lib, _problem(hkv=3), m, bws, 1 << 40) == B.ATTN_ERR_SHAPE
 
 
 def test_dense_mask_arguments():

@@ -138,3 +138,22 @@ def test_workspace_must_be_contiguous():
     q, k, v = _qkv()
     ws = torch.zeros(1024, dtype=torch.uint8)[::2]
     _fwd_raises(ValueError, q, k, v, workspace=ws)
+
+
+def test_backward_plan_arguments():
+    q, k, v = _qkv()
+    ws = torch.zeros(1 << 16, dtype=torch.uint8)
+    # the planned forward takes the library's own key-range split
+    with pytest.raises(ValueError, match="kv_splits"):
+        B.attn_fwd(q, k, v, kv_splits=2, bwd_plan=ws)
+    # a non-contiguous plan workspace
+    with pytest.raises(ValueError, match="contiguous"):
+        B.attn_fwd(q, k, v, bwd_plan=torch.zeros(2, 1 << 15, dtype=torch.uint8).t())
+    # a planned backward needs the workspace the forward planned into
+    with pytest.raises(ValueError, match="planned"):
+        B.attn_bwd(**_bwd_args(), planned=True)
+    # valid arguments on CPU tensors still stop at the device check
+    with pytest.raises(ValueError, match="GPU"):
+        B.attn_fwd(q, k, v, bwd_plan=ws)
+    with pytest.raises(ValueError, match="GPU"):
+        B.attn_bwd(**_bwd_args(), workspace=ws, planned=True)
