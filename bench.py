@@ -305,7 +305,7 @@ def run_gpu(args):
     # come before the caller's warm-up steps, so that a short run (few warm-up and timed steps)
     # measures the same steady state as a long one.
     settle_steps = 0
-    settle_end = time.perf_counter() + SETTLE_S
+    settle_end = time.perf_counter() + args.settle_s
     while time.perf_counter() < settle_end:
         step()
         settle_steps += 1
@@ -398,7 +398,7 @@ def run_gpu(args):
         },
         "pct_of_bf16_mfma_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "wall_s_timed": round(wall, 4),
-        "settle": {"seconds": SETTLE_S, "steps": settle_steps, "note": "untimed steps before the warm-up steps"},
+        "settle": {"seconds": args.settle_s, "steps": settle_steps, "note": "untimed steps before the warm-up steps"},
         "roofline": roofline,
         "workloads": workloads,
     }
@@ -769,6 +769,9 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--settle-s", type=float, default=SETTLE_S,
+                    help="seconds of untimed steps before the warm-up steps (0 for counter runs, whose "
+                         "per-dispatch records the settling steps would multiply)")
     ap.add_argument("--all", action="store_true", help="also print forward timings of every workload to stderr")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed steps, run one device copy of this many MiB (counter calibration)")
