@@ -209,16 +209,27 @@ int32_t fwd_splits(const attn_problem* p, const attn_mask* m, int32_t requested)
 }
 
 struct FwdSizes {
-  size_t plan_bytes, dense_off, o_part_off, lse_part_off, total;
+  size_t plan_bytes, pairs_off, pairs_bytes, dense_off, o_part_off, lse_part_off, total;
   DenseSizes dense;
 };
 
-// Forward workspace: planner items, packed dense mask, split-KV partials.
+// Whether the forward's planner pairs layout rows into its 128-row query tiles (bf16 inputs, a
+// block layout shared by every (batch, head); see plan_pairs_rows).
+bool fwd_pairs_rows(const attn_problem* p, const attn_mask* m) {
+  if (p->dtype != ATTN_BF16 || m->kind != ATTN_MASK_BLOCK) return false;
+  const int bm = fwd_tile_m(p, m);
+  return plan_pairs_rows(MASK_BLOCK, m->layout_stride_b, m->layout_stride_h, bm, ceil_div(p->seq_q, bm),
+                         ceil_div(p->seq_q, 64), ceil_div(p->seq_k, 64));
+}
+
+// Forward workspace: planner items, the planner's row pairs, packed dense mask, split-KV partials.
 FwdSizes fwd_sizes(const attn_problem* p, const attn_mask* m, int32_t splits) {
   FwdSizes z{};
   z.plan_bytes = fwd_needs_plan(p, m) ? align_up((size_t)fwd_items(p, m) * 4) : 0;
+  z.pairs_off = z.plan_bytes;
+  z.pairs_bytes = fwd_pairs_rows(p, m) ? align_up((size_t)ceil_div(p->seq_q, fwd_tile_m(p, m)) * 4) : 0;
   z.dense = dense_sizes(p, m, false);
-  z.dense_off = z.plan_bytes;
+  z.dense_off = z.pairs_off + z.pairs_bytes;
   z.o_part_off = z.lse_part_off = z.total = z.dense_off + z.dense.total;
   if (splits > 1) {
     const size_t rows = (size_t)p->batch * p->heads_q * p->seq_q;
@@ -239,7 +250,8 @@ struct BwdSizes {
   int dkdv;    // dK/dV kernel variant (DKDV_*)
   int bq, bk, n_qt, n_kt;
   int64_t q_items, kv_items;
-  size_t delta_off, lse2_off, sseed_off, kv_off, q_off, dq_acc_off, dense_off, total;
+  size_t delta_off, lse2_off, sseed_off, kv_off, q_off, pairs_off, dq_acc_off, dense_off, total;
+  bool pairs;  // the dQ list pairs layout rows (see plan_pairs_rows)
   DenseSizes dense;
 };
 
@@ -259,12 +271,21 @@ BwdSizes bwd_sizes(const attn_problem* p, const attn_mask* m, int32_t flags = 0)
   s.sseed_off = s.lse2_off + align_up((size_t)p->batch * p->heads_q * p->seq_q * 4);
   s.kv_off = s.sseed_off + (s.dkdv != DKDV_ONE_WAVE ? align_up((size_t)p->batch * p->heads_q * p->seq_q * 4) : 0);
   s.q_off = s.kv_off + align_up((size_t)s.kv_items * 4);
+  s.pairs = false;
+  s.pairs_off = 0;
   if (flags & ATTN_BWD_ATOMIC_DQ) {
     s.dq_acc_off = s.q_off;
     s.total = s.dq_acc_off + align_up((size_t)p->batch * p->heads_q * p->seq_q * p->head_dim * 4);
   } else {
     s.dq_acc_off = 0;
     s.total = s.q_off + align_up((size_t)s.q_items * 4);
+    s.pairs = m->kind == ATTN_MASK_BLOCK &&
+              plan_pairs_rows(MASK_BLOCK, m->layout_stride_b, m->layout_stride_h, s.bq, s.n_qt, ceil_div(p->seq_q, 64),
+                              ceil_div(p->seq_k, 64));
+    if (s.pairs) {
+      s.pairs_off = s.total;
+      s.total += align_up((size_t)s.n_qt * 4);
+    }
   }
   // a dense mask's bits (rows and columns) and block layout follow
   s.dense = dense_sizes(p, m, true);
@@ -310,6 +331,7 @@ void bwd_plan_params(const attn_problem* p, const attn_mask* m, const BwdSizes& 
   pk->n_items = (int32_t)bs.kv_items; pk->items = (uint32_t*)(ws + bs.kv_off);
   pq->mode = PLAN_FWD_Q; pq->heads = p->heads_q; pq->n_tiles = bs.n_qt; pq->tile = bs.bq;
   pq->n_items = (int32_t)bs.q_items; pq->items = (uint32_t*)(ws + bs.q_off);
+  pq->row_pairs = bs.pairs ? (uint16_t*)(ws + bs.pairs_off) : nullptr;
 }
 
 attn_status hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
@@ -544,11 +566,13 @@ attn_status fwd_call(const attn_problem* problem, const void* Q, const void* K, 
     pp.layout_stride_b = fp.layout_stride_b; pp.layout_stride_h = fp.layout_stride_h;
     pp.items = (uint32_t*)workspace;
     pp.n_xcd = fp.n_xcd;
+    pp.row_pairs = fz.pairs_bytes > 0 ? (uint16_t*)((char*)workspace + fz.pairs_off) : nullptr;
     st = hip_status(timed(ATTN_KERNEL_PLAN, s, [&] {
       return plan_bwd ? launch_plan_triple(pp, pk, pq, s) : launch_plan(pp, s);
     }));
     if (st != ATTN_OK) return st;
     fp.items = (const uint32_t*)workspace;
+    fp.row_pairs = pp.row_pairs;
   } else if (plan_bwd) {
     // the forward orders its items in closed form; the backward's lists still need a launch
     st = hip_status(timed(ATTN_KERNEL_PLAN, s, [&] { return launch_plan_pair(pk, pq, s); }));
@@ -662,6 +686,7 @@ attn_status bwd_call(const attn_problem* problem, const void* Q, const void* K, 
   bp.layout_stride_b = m->layout_stride_b; bp.layout_stride_h = m->layout_stride_h;
   bp.items_kv = (const uint32_t*)(ws + bs.kv_off);
   bp.items_q = (const uint32_t*)(ws + bs.q_off);
+  bp.row_pairs = bs.pairs ? (const uint16_t*)(ws + bs.pairs_off) : nullptr;
   bp.batch = p->batch; bp.heads_q = p->heads_q; bp.heads_kv = p->heads_kv;
   bp.seq_q = p->seq_q; bp.seq_k = p->seq_k;
   bp.group = p->heads_q / p->heads_kv;

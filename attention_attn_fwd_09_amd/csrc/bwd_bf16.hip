@@ -1013,7 +1013,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
   const Item it = decode_item(item, p.heads_q, p.n_qtiles);
   const int b = it.b, h = it.h, kvh = h / p.group;
   const int q0 = it.t * BM;
-  const int qw0 = q0 + wave * 32;
+  // the 32 query rows of this wave: waves 0-1 cover the tile's first layout row, 2-3 its second
+  // (under a block layout, the two rows the planner paired for the tile)
+  const int qw0 = (MASK == MASK_BLOCK && BM == 128) ? tile_row(p.row_pairs, it.t, wave >> 1) * 64 + (wave & 1) * 32
+                                                    : q0 + wave * 32;
   const int my_q = qw0 + c;
 
   const size_t q_off = ((size_t)(b * p.heads_q + h) * p.seq_q) * D;
@@ -1055,7 +1058,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
         if (j < p.nb_k) {
 #pragma unroll
           for (int r = 0; r < ROWS; ++r) {
-            const int row = r0 + r;
+            const int row = ROWS == 2 ? tile_row(p.row_pairs, r0 / 2, r) : r0 + r;
             if (row < p.nb_q && lay[(size_t)row * p.nb_k + j] != 0) bits |= 1u << r;
           }
         }

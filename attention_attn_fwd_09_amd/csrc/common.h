@@ -129,6 +129,12 @@ __device__ __forceinline__ float partner_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Layout row r (0 or 1) of 128-row query tile t: rows 2t and 2t + 1, or the two rows the planner
+// paired for the tile (row_pairs[2t + r]). A row index of nb_q or more names no row.
+__device__ __forceinline__ int tile_row(const uint16_t* row_pairs, int t, int r) {
+  return row_pairs != nullptr ? (int)row_pairs[2 * t + r] : 2 * t + r;
+}
+
 // --- item encoding: item = (b * heads_q + h) * n_qtiles + qtile ---
 struct Item {
   int b, h, t;

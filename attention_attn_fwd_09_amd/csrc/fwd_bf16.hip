@@ -79,7 +79,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
   }
   const int b = it.b, h = it.h, kvh = h / p.group;
   const int q0 = it.t * BM;
-  const int qw0 = q0 + wave * 32;
+  // the 32 query rows of this wave: waves 0-1 cover the tile's first layout row, 2-3 its second
+  // (under a block layout, the two rows the planner paired for the tile)
+  const int qw0 = (MASK == MASK_BLOCK && BM == 128) ? tile_row(p.row_pairs, it.t, wave >> 1) * 64 + (wave & 1) * 32
+                                                    : q0 + wave * 32;
   const int my_q = qw0 + c;
   // dense mask: this query's row of bits (only read when MASK_DENSE)
   const uint32_t* dense_row = MASK == MASK_DENSE

@@ -11,8 +11,9 @@ namespace attn {
 //  * NONE: every tile of the keys; CAUSAL: tiles up to the item's last query;
 //  * PADDING: tiles of the batch element's valid length (none for a fully padded query tile);
 //  * BLOCK / DENSE: the kept tiles of the layout rows the item covers (a dense mask through its
-//    derived layout), listed by wave 0 into `list` with one bit per covered 64-row layout row
-//    (bits << 16 | key tile); list[max_list] holds the count.
+//    derived layout; for 128-row tiles the two rows tile_row names), listed by wave 0 into `list`
+//    with one bit per covered 64-row layout row (bits << 16 | key tile); list[max_list] holds the
+//    count.
 // kv_len / q_len: keys at or beyond kv_len are hidden; queries at or beyond q_len see nothing.
 // Every thread of the workgroup must call this (the list is published with a barrier).
 template <int MASK, int BM, int BN>
@@ -39,7 +40,7 @@ __device__ __forceinline__ int fwd_key_tiles(const FwdParams& p, int b, int h, i
         if (j < p.nb_k) {
 #pragma unroll
           for (int r = 0; r < ROWS; ++r) {
-            const int row = r0 + r;
+            const int row = ROWS == 2 ? tile_row(p.row_pairs, r0 / 2, r) : r0 + r;
             if (row < p.nb_q && lay[(size_t)row * p.nb_k + j] != 0) bits |= 1u << r;
           }
         }

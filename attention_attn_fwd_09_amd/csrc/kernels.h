@@ -4,10 +4,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-namespace attn {
+#include "params.h"
 
-struct FwdParams;
-struct BwdParams;
+namespace attn {
 
 enum PlanMode : int { PLAN_FWD_Q = 0, PLAN_BWD_KV = 1 };
 
@@ -27,9 +26,20 @@ struct PlanParams {
   int64_t layout_stride_b, layout_stride_h;
   int32_t n_xcd;         // XCDs workgroups are dealt to round robin (at most kMaxXcd; 1 = no grouping)
   uint32_t* items;       // output: item ids, longest first
+  uint16_t* row_pairs;   // output (query tiles of two layout rows, when plan_pairs_rows holds): the two
+                         //   rows of tile t are row_pairs[2t], row_pairs[2t + 1]; nb_q = no row. Else null
 };
 
 constexpr int kMaxXcd = 8;   // XCDs the planner can group items for
+
+// Whether a query-tile list pairs its layout rows by shared kept tiles instead of taking rows 2t
+// and 2t + 1: a block layout shared by every (batch, head), of at most 64 rows and 64 key tiles
+// per row, with 128-row query tiles (two layout rows each). Host and device decide alike.
+__host__ __device__ inline bool plan_pairs_rows(int mask, int64_t layout_stride_b, int64_t layout_stride_h, int tile,
+                                                int n_tiles, int nb_q, int nb_k) {
+  return mask == MASK_BLOCK && layout_stride_b == 0 && layout_stride_h == 0 && tile == 128 && nb_k <= 64 &&
+         nb_q <= 64 && n_tiles == (nb_q + 1) / 2;
+}
 
 // Dense element mask -> row bits, column bits (optional) and a 64x64 block layout.
 struct DensePackParams {

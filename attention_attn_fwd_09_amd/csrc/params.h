@@ -30,6 +30,8 @@ struct FwdParams {
   const uint8_t* layout;        // BLOCK
   int64_t layout_stride_b, layout_stride_h;
   const uint32_t* items;        // planner output (PADDING/BLOCK), else null
+  const uint16_t* row_pairs;    // planner output: the two layout rows of each 128-row query tile, or
+                                //   null for rows 2t, 2t + 1
   int32_t batch, heads_q, heads_kv, seq_q, seq_k;
   int32_t group;                // heads_q / heads_kv
   int32_t n_qtiles;             // ceil(seq_q / BM)
@@ -69,6 +71,7 @@ struct BwdParams {
   int64_t layout_stride_b, layout_stride_h;
   const uint32_t* items_kv;     // planner output for the dK/dV pass
   const uint32_t* items_q;      // planner output for the dQ pass
+  const uint16_t* row_pairs;    // planner output: the two layout rows of each dQ query tile, or null
   int32_t batch, heads_q, heads_kv, seq_q, seq_k;
   int32_t group;
   int32_t n_qtiles, n_ktiles;

@@ -70,7 +70,7 @@ __device__ int layout_col_union_count(const uint8_t* lay, int nb_k, int c0, int 
 constexpr int MAX_UNITS = 4096;   // tiles whose cost is tabulated once in LDS (shared block layouts)
 constexpr int MAX_LENGTHS = 4096; // padding lengths cached in LDS
 
-struct PlanShared {
+struct alignas(16) PlanShared {
   int unit_cost[MAX_UNITS];       // shared block layout: kept tiles per layout row (or column)
   int lengths[MAX_LENGTHS];
 };
@@ -156,7 +156,112 @@ __device__ __forceinline__ bool closed_form_plan(const PlanParams& p) {
          p.n_tiles <= MAX_RANKED && (int64_t)p.nb_q * p.nb_k <= MAX_STAGED_LAYOUT;
 }
 
-__device__ __forceinline__ void plan_closed_form(const PlanParams& p, uint8_t* lay, int* cost, int* order) {
+// Pairs the nb_q (at most 64) rows of a shared layout into query tiles of two (plan_pairs_rows): in
+// rounds, every open row names the open row it shares the most kept tiles with (ties to the lower
+// index), and rows that name each other pair. Each round pairs at least one pair (the pair of
+// largest overlap with the lowest indices names itself both ways). After MAX_PAIR_ROUNDS rounds,
+// or once no pair forms, the open rows pair in index order, an odd last one with "no row" (nb_q).
+// Tile t is the pair whose lower row is the t-th lowest; its cost is the number of kept tiles in
+// the union of its two rows. Writes p.row_pairs and cost[0, n_tiles).
+//
+// Lane r of every wave stands for row r. Waves 0-3 (one per SIMD) hold the keys
+// (overlap << 16 | 0xffff - t) of their row against sixteen candidates each and, every round, post
+// the best open one; after one barrier every wave takes the best of the four posts of each row and
+// finds the mutual choices with one lane exchange, so all waves hold the same open rows without a
+// second barrier (the posts of consecutive rounds go to alternate buffers).
+constexpr int MAX_PAIR_ROUNDS = 6;
+constexpr int MAX_PAIR_ROWS = 64;                        // layout rows the pairing handles (plan_pairs_rows)
+constexpr int PAIR_WAVES = 4;                            // waves that scan candidates
+constexpr int PAIR_CANDS = MAX_PAIR_ROWS / PAIR_WAVES;   // candidates per scanning wave
+static_assert(MAX_PAIR_ROWS == 4 * (THREADS / 64), "every wave computes the keys of four candidates");
+static_assert(MAX_RANKED + MAX_PAIR_ROWS * MAX_PAIR_ROWS <= NBUCKET, "the keys follow the ranked order in the buckets");
+
+struct PairLds {
+  uint64_t mask[MAX_PAIR_ROWS];                  // kept key tiles of each row, one bit each
+  int partial[2][PAIR_WAVES][MAX_PAIR_ROWS];     // best key of each row among each wave's candidates
+};
+
+__device__ void pair_rows(const PlanParams& p, const uint8_t* lay, PairLds& s, int* keys, int* cost) {
+  constexpr int NW = THREADS / 64;
+  const int nq = p.nb_q;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // row masks: wave w builds rows w + 16 i, one lane per key tile (nb_k <= 64); loads first
+  uint8_t kept[MAX_PAIR_ROWS / NW];
+#pragma unroll
+  for (int i = 0; i < MAX_PAIR_ROWS / NW; ++i) {
+    const int r = wave + NW * i;
+    kept[i] = (r < nq && lane < p.nb_k) ? lay[r * p.nb_k + lane] : 0;
+  }
+#pragma unroll
+  for (int i = 0; i < MAX_PAIR_ROWS / NW; ++i) {
+    const int r = wave + NW * i;
+    const uint64_t m = __ballot(kept[i] != 0);
+    if (lane == 0 && r < nq) s.mask[r] = m;
+  }
+  __syncthreads();
+  // keys: wave w computes candidates 4w .. 4w + 3 for every row into keys[t][r]; the scanning
+  // waves then load their sixteen
+  const int r = lane;
+  const uint64_t own = r < nq ? s.mask[r] : 0ull;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int t = 4 * wave + j;
+    keys[t * MAX_PAIR_ROWS + r] =
+        (t < nq && r < nq && t != r) ? (__popcll(own & s.mask[t]) << 16) | (0xffff - t) : -1;
+  }
+  __syncthreads();
+  const bool scan = wave < PAIR_WAVES;
+  int key[PAIR_CANDS];
+#pragma unroll
+  for (int j = 0; j < PAIR_CANDS; ++j) key[j] = scan ? keys[(PAIR_CANDS * wave + j) * MAX_PAIR_ROWS + r] : -1;
+  uint64_t open = nq >= 64 ? ~0ull : (1ull << nq) - 1;   // rows not yet paired (the same in every wave)
+  int partner = -1;                                       // the row paired with row r
+  for (int round = 0; round < MAX_PAIR_ROUNDS; ++round) {
+    if (scan) {
+      int post = -1;
+#pragma unroll
+      for (int j = 0; j < PAIR_CANDS; ++j)
+        if ((open >> (PAIR_CANDS * wave + j)) & 1) post = max(post, key[j]);
+      s.partial[round & 1][wave][r] = post;
+    }
+    __syncthreads();
+    int k = -1;
+#pragma unroll
+    for (int w = 0; w < PAIR_WAVES; ++w) k = max(k, s.partial[round & 1][w][r]);
+    const int b = (((open >> r) & 1) && k >= 0) ? 0xffff - (k & 0xffff) : -1;
+    const int bb = __shfl(b, b >= 0 ? b : r, 64);   // the choice of row b
+    const bool mutual = b >= 0 && bb == r;
+    if (mutual) partner = b;
+    open = __ballot(r < nq && partner < 0);
+    if (__ballot(mutual) == 0) break;
+  }
+  if (wave == 0) {
+    // the rows still open pair in index order, an odd last one with "no row"
+    const uint64_t below = r == 0 ? 0ull : open & (~0ull >> (64 - r));   // open rows under r
+    if ((open >> r) & 1) {
+      if (__popcll(below) & 1) {
+        partner = 63 - __builtin_clzll(below);
+      } else {
+        const uint64_t above = r == 63 ? 0ull : open & (~0ull << (r + 1));
+        partner = above != 0 ? __builtin_ctzll(above) : nq;
+      }
+    }
+    // tiles in order of their lower row
+    const bool first = r < nq && partner > r;
+    const uint64_t firsts = __ballot(first);
+    if (first) {
+      const int t = __popcll(r == 0 ? 0ull : firsts & (~0ull >> (64 - r)));
+      p.row_pairs[2 * t] = (uint16_t)r;
+      p.row_pairs[2 * t + 1] = (uint16_t)partner;
+      cost[t] = __popcll(own | (partner < nq ? s.mask[partner] : 0ull));
+    }
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ void plan_closed_form(const PlanParams& p, uint8_t* lay, int* cost, int* order,
+                                                 PairLds& pair_lds) {
   const int nbytes = p.nb_q * p.nb_k;
   if ((reinterpret_cast<uintptr_t>(p.layout) & 15) == 0) {
     // 16 bytes per thread (the LDS copy is 16-byte aligned); the tail byte by byte
@@ -169,21 +274,25 @@ __device__ __forceinline__ void plan_closed_form(const PlanParams& p, uint8_t* l
   }
   for (int t = threadIdx.x; t < p.n_tiles; t += THREADS) cost[t] = 0;
   __syncthreads();
-  // kept tiles in the union of each tile's layout rows (columns): one (tile, column) pair per thread
-  const int per_unit = p.tile / 64;   // layout rows (query tiles) or columns (key tiles) per tile
-  const int n_other = p.mode == PLAN_BWD_KV ? p.nb_q : p.nb_k;
-  const int pairs = p.n_tiles * n_other;
-  for (int e = threadIdx.x; e < pairs; e += THREADS) {
-    const int t = e / n_other, x = e - t * n_other;
-    bool keep = false;
-    for (int r = 0; r < per_unit; ++r) {
-      const int y = t * per_unit + r;
-      if (p.mode == PLAN_BWD_KV) keep = keep || (y < p.nb_k && lay[x * p.nb_k + y] != 0);
-      else keep = keep || (y < p.nb_q && lay[y * p.nb_k + x] != 0);
+  if (p.row_pairs != nullptr) {
+    pair_rows(p, lay, pair_lds, order + MAX_RANKED, cost);
+  } else {
+    // kept tiles in the union of each tile's layout rows (columns): one (tile, column) pair per thread
+    const int per_unit = p.tile / 64;   // layout rows (query tiles) or columns (key tiles) per tile
+    const int n_other = p.mode == PLAN_BWD_KV ? p.nb_q : p.nb_k;
+    const int pairs = p.n_tiles * n_other;
+    for (int e = threadIdx.x; e < pairs; e += THREADS) {
+      const int t = e / n_other, x = e - t * n_other;
+      bool keep = false;
+      for (int r = 0; r < per_unit; ++r) {
+        const int y = t * per_unit + r;
+        if (p.mode == PLAN_BWD_KV) keep = keep || (y < p.nb_k && lay[x * p.nb_k + y] != 0);
+        else keep = keep || (y < p.nb_q && lay[y * p.nb_k + x] != 0);
+      }
+      if (keep) atomicAdd(&cost[t], 1);
     }
-    if (keep) atomicAdd(&cost[t], 1);
+    __syncthreads();
   }
-  __syncthreads();
   // rank of each tile, longest first and ties by index: one wave per tile, 64 comparisons a ballot
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int t = wave; t < p.n_tiles; t += THREADS / 64) {
@@ -218,7 +327,9 @@ __device__ __forceinline__ void plan_items(const PlanParams& p) {
   __shared__ __attribute__((aligned(16))) uint16_t cached[MAX_CACHED];
   __shared__ PlanShared sh;
   if (closed_form_plan(p)) {
-    plan_closed_form(p, (uint8_t*)cached, sh.unit_cost, bucket);
+    // the row pairing works in the padding-length cache
+    static_assert(sizeof(PairLds) <= sizeof(sh.lengths) && offsetof(PlanShared, lengths) % 8 == 0, "pairing LDS");
+    plan_closed_form(p, (uint8_t*)cached, sh.unit_cost, bucket, *reinterpret_cast<PairLds*>(sh.lengths));
     return;
   }
   const bool cache = p.n_items <= MAX_CACHED;

@@ -9,6 +9,7 @@ skipped, or written twice in place of another, fails the comparison.
 """
 
 import pytest
+import torch
 
 import oracle
 from attention_attn_fwd_09_amd import binding as libattn
@@ -79,4 +80,43 @@ def test_bwd_xcd_grouped_order(gpu_available, case):
     grads = bwd_into_nan(w, inp, o, lse, flags=flags)
     ref = oracle.attention_bwd(to_np64(inp["q"]), to_np64(inp["k"]), to_np64(inp["v"]), to_np64(inp["do"]),
                                oracle_mask(w, inp), inp["scale"])
+    check_grads(tuple(to_np64(g) for g in grads), ref, str(case))
+
+
+def _paired_layout(nbq: int, nbk: int) -> torch.Tensor:
+    """A shared block layout whose rows overlap most with rows far from them: row r keeps the key
+    tiles (7 (r mod 16) + 5 j) mod nbk for j < 4 and its diagonal tile, and every ninth row keeps
+    none. Pairing rows by shared kept tiles then differs from pairing rows 2t and 2t + 1."""
+    lay = torch.zeros(nbq, nbk, dtype=torch.uint8)
+    for r in range(nbq):
+        if r % 9 == 4:
+            continue
+        for j in range(4):
+            lay[r, (7 * (r % 16) + 5 * j) % nbk] = 1
+        if r < nbk:
+            lay[r, r] = 1
+    return lay
+
+
+# (head_dim, seq): 3, 63 (odd, ragged) and 64 layout rows are paired by overlap; 65 rows take
+# rows 2t and 2t + 1
+PAIRED = ((64, 150), (128, 4022), (64, 4096), (64, 4100))
+
+
+@pytest.mark.parametrize("case", PAIRED, ids=lambda c: "-".join(map(str, c)))
+def test_block_rows_paired_by_overlap(gpu_available, case):
+    """Forward and two-pass backward under a shared block layout whose 128-row query tiles take
+    the two layout rows the planner pairs by shared kept tiles (the kernels look the rows up per
+    tile), against the oracle element by element, into NaN-filled outputs."""
+    d, s = case
+    w = _w("bf16", d, "block", 1, 2, 1, s, backward=True)
+    inp = make_inputs(w, 1300 + s + d)
+    inp["layout"] = _paired_layout(-(-s // 64), -(-s // 64))
+    say(f"block rows paired by overlap {case}")
+    o, lse = fwd_into_nan(w, inp)
+    q, k, v = to_np64(inp["q"]), to_np64(inp["k"]), to_np64(inp["v"])
+    o_ref, lse_ref = oracle.attention_fwd(q, k, v, oracle_mask(w, inp), inp["scale"])
+    compare_fwd(to_np64(o), to_np64(lse), o_ref, lse_ref, TOL_BF16_FWD, str(case))
+    grads = bwd_into_nan(w, inp, o, lse)
+    ref = oracle.attention_bwd(q, k, v, to_np64(inp["do"]), oracle_mask(w, inp), inp["scale"])
     check_grads(tuple(to_np64(g) for g in grads), ref, str(case))
