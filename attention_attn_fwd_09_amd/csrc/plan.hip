@@ -144,6 +144,22 @@ __device__ int block_exclusive_scan(int v, int* wave_sums) {
   return wave_sums[wave] + incl - v;
 }
 
+// q = a / b and rem = a % b for 0 <= a < 2^24 and b >= 1, from inv_b = 1/b in float: the product
+// a * inv_b is within one of the quotient, which the remainder's range then corrects.
+__device__ __forceinline__ int divmod_small(int a, int b, float inv_b, int& rem) {
+  int q = (int)((float)a * inv_b);
+  int r = a - q * b;
+  if (r < 0) {
+    --q;
+    r += b;
+  } else if (r >= b) {
+    ++q;
+    r -= b;
+  }
+  rem = r;
+  return q;
+}
+
 // Closed-form list for a block layout shared by every (batch, head): all units have the same
 // per-tile costs, so the tiles are ranked once (longest first, ties by index) and the list is
 // rank-major, unit-minor, with unit u on XCD u % n_xcd (list positions slot * n_xcd + xcd). The
@@ -181,25 +197,29 @@ struct PairLds {
   int partial[2][PAIR_WAVES][MAX_PAIR_ROWS];     // best key of each row among each wave's candidates
 };
 
-__device__ void pair_rows(const PlanParams& p, const uint8_t* lay, PairLds& s, int* keys, int* cost) {
+__device__ void pair_rows(const PlanParams& p, const uint8_t* lay, bool masks_ready, PairLds& s, int* keys,
+                          int* cost) {
   constexpr int NW = THREADS / 64;
   const int nq = p.nb_q;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // row masks: wave w builds rows w + 16 i, one lane per key tile (nb_k <= 64); loads first
-  uint8_t kept[MAX_PAIR_ROWS / NW];
+  // row masks (unless the layout copy wrote them): wave w builds rows w + 16 i, one lane per key
+  // tile (nb_k <= 64); loads first
+  if (!masks_ready) {
+    uint8_t kept[MAX_PAIR_ROWS / NW];
 #pragma unroll
-  for (int i = 0; i < MAX_PAIR_ROWS / NW; ++i) {
-    const int r = wave + NW * i;
-    kept[i] = (r < nq && lane < p.nb_k) ? lay[r * p.nb_k + lane] : 0;
-  }
+    for (int i = 0; i < MAX_PAIR_ROWS / NW; ++i) {
+      const int r = wave + NW * i;
+      kept[i] = (r < nq && lane < p.nb_k) ? lay[r * p.nb_k + lane] : 0;
+    }
 #pragma unroll
-  for (int i = 0; i < MAX_PAIR_ROWS / NW; ++i) {
-    const int r = wave + NW * i;
-    const uint64_t m = __ballot(kept[i] != 0);
-    if (lane == 0 && r < nq) s.mask[r] = m;
+    for (int i = 0; i < MAX_PAIR_ROWS / NW; ++i) {
+      const int r = wave + NW * i;
+      const uint64_t m = __ballot(kept[i] != 0);
+      if (lane == 0 && r < nq) s.mask[r] = m;
+    }
+    __syncthreads();
   }
-  __syncthreads();
   // keys: wave w computes candidates 4w .. 4w + 3 for every row into keys[t][r]; the scanning
   // waves then load their sixteen
   const int r = lane;
@@ -263,11 +283,31 @@ __device__ void pair_rows(const PlanParams& p, const uint8_t* lay, PairLds& s, i
 __device__ __forceinline__ void plan_closed_form(const PlanParams& p, uint8_t* lay, int* cost, int* order,
                                                  PairLds& pair_lds) {
   const int nbytes = p.nb_q * p.nb_k;
-  if ((reinterpret_cast<uintptr_t>(p.layout) & 15) == 0) {
+  const bool aligned = (reinterpret_cast<uintptr_t>(p.layout) & 15) == 0;
+  // with row pairing on whole 16-byte row chunks, the copy also writes the rows' kept-tile masks
+  // (16 bits per chunk, upper chunks past nb_k zero)
+  const bool masks_in_copy = p.row_pairs != nullptr && aligned && (p.nb_k & 15) == 0;
+  if (aligned) {
     // 16 bytes per thread (the LDS copy is 16-byte aligned); the tail byte by byte
     const int n16 = nbytes / 16;
-    for (int i = threadIdx.x; i < n16; i += THREADS)
-      reinterpret_cast<uint4*>(lay)[i] = reinterpret_cast<const uint4*>(p.layout)[i];
+    const int chunks = p.nb_k / 16;   // per row, when masks_in_copy
+    const float i_chunks = 1.0f / (float)max(chunks, 1);
+    uint16_t* mask16 = reinterpret_cast<uint16_t*>(pair_lds.mask);
+    for (int i = threadIdx.x; i < n16; i += THREADS) {
+      const uint4 v = reinterpret_cast<const uint4*>(p.layout)[i];
+      reinterpret_cast<uint4*>(lay)[i] = v;
+      if (masks_in_copy) {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        uint32_t bits = 0;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) bits |= (((w[k >> 2] >> ((k & 3) * 8)) & 0xffu) != 0u ? 1u : 0u) << k;
+        int chunk;
+        const int row = divmod_small(i, chunks, i_chunks, chunk);
+        mask16[row * 4 + chunk] = (uint16_t)bits;
+        if (chunk == chunks - 1)
+          for (int c2 = chunks; c2 < 4; ++c2) mask16[row * 4 + c2] = 0;
+      }
+    }
     for (int i = n16 * 16 + threadIdx.x; i < nbytes; i += THREADS) lay[i] = p.layout[i];
   } else {
     for (int i = threadIdx.x; i < nbytes; i += THREADS) lay[i] = p.layout[i];
@@ -275,7 +315,7 @@ __device__ __forceinline__ void plan_closed_form(const PlanParams& p, uint8_t* l
   for (int t = threadIdx.x; t < p.n_tiles; t += THREADS) cost[t] = 0;
   __syncthreads();
   if (p.row_pairs != nullptr) {
-    pair_rows(p, lay, pair_lds, order + MAX_RANKED, cost);
+    pair_rows(p, lay, masks_in_copy, pair_lds, order + MAX_RANKED, cost);
   } else {
     // kept tiles in the union of each tile's layout rows (columns): one (tile, column) pair per thread
     const int per_unit = p.tile / 64;   // layout rows (query tiles) or columns (key tiles) per tile
@@ -312,12 +352,26 @@ __device__ __forceinline__ void plan_closed_form(const PlanParams& p, uint8_t* l
   const int heads_kv = p.heads / G;
   const int n_xcd = (p.n_xcd > 1 && p.n_xcd <= kMaxXcd && n_units % p.n_xcd == 0) ? p.n_xcd : 1;
   const int per_rank = (n_units / n_xcd) * G;
-  for (int pos = threadIdx.x; pos < p.n_items; pos += THREADS) {
-    const int x = pos % n_xcd, slot = pos / n_xcd;
-    const int r = slot / per_rank, rem = slot - r * per_rank;
-    const int u = x + n_xcd * (rem / G);
-    const int b = u / heads_kv, h = (u - b * heads_kv) * G + rem % G;
-    p.items[pos] = (uint32_t)(((int64_t)b * p.heads + h) * p.n_tiles + order[r]);
+  if (p.n_items < (1 << 24)) {
+    // the four divisions by workgroup-uniform divisors through float reciprocals
+    const float i_xcd = 1.0f / (float)n_xcd, i_rank = 1.0f / (float)per_rank, i_g = 1.0f / (float)G,
+                i_hkv = 1.0f / (float)heads_kv;
+    for (int pos = threadIdx.x; pos < p.n_items; pos += THREADS) {
+      int x, rem, g, hk;
+      const int slot = divmod_small(pos, n_xcd, i_xcd, x);
+      const int r = divmod_small(slot, per_rank, i_rank, rem);
+      const int u = x + n_xcd * divmod_small(rem, G, i_g, g);
+      const int b = divmod_small(u, heads_kv, i_hkv, hk);
+      p.items[pos] = (uint32_t)(((int64_t)b * p.heads + hk * G + g) * p.n_tiles + order[r]);
+    }
+  } else {
+    for (int pos = threadIdx.x; pos < p.n_items; pos += THREADS) {
+      const int x = pos % n_xcd, slot = pos / n_xcd;
+      const int r = slot / per_rank, rem = slot - r * per_rank;
+      const int u = x + n_xcd * (rem / G);
+      const int b = u / heads_kv, h = (u - b * heads_kv) * G + rem % G;
+      p.items[pos] = (uint32_t)(((int64_t)b * p.heads + h) * p.n_tiles + order[r]);
+    }
   }
 }
 
@@ -408,16 +462,15 @@ __device__ __forceinline__ void plan_items(const PlanParams& p) {
 
 __global__ __launch_bounds__(THREADS) void plan_kernel(PlanParams p) { plan_items(p); }
 
-// Two independent item lists (the backward's dK/dV and dQ lists) in one launch, one workgroup each.
-__global__ __launch_bounds__(THREADS) void plan_pair_kernel(PlanParams a, PlanParams b) {
-  plan_items(blockIdx.x == 0 ? a : b);
-}
-
-// Three lists in one launch: the forward's and the backward's two, when a forward also plans the
-// backward that follows it.
-__global__ __launch_bounds__(THREADS) void plan_triple_kernel(PlanParams a, PlanParams b, PlanParams c) {
-  plan_items(blockIdx.x == 0 ? a : (blockIdx.x == 1 ? b : c));
-}
+// Several independent item lists in one launch, one workgroup each: the backward's dK/dV and dQ
+// lists, and with them the forward's when a forward also plans the backward that follows it. The
+// workgroup reads its list's parameters in place from the kernel arguments.
+template <int N>
+struct PlanList {
+  PlanParams p[N];
+};
+__global__ __launch_bounds__(THREADS) void plan_pair_kernel(PlanList<2> lists) { plan_items(lists.p[blockIdx.x]); }
+__global__ __launch_bounds__(THREADS) void plan_triple_kernel(PlanList<3> lists) { plan_items(lists.p[blockIdx.x]); }
 
 }  // namespace
 
@@ -427,12 +480,12 @@ hipError_t launch_plan(const PlanParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_plan_pair(const PlanParams& a, const PlanParams& b, hipStream_t stream) {
-  hipLaunchKernelGGL(plan_pair_kernel, dim3(2), dim3(THREADS), 0, stream, a, b);
+  hipLaunchKernelGGL(plan_pair_kernel, dim3(2), dim3(THREADS), 0, stream, PlanList<2>{{a, b}});
   return hipGetLastError();
 }
 
 hipError_t launch_plan_triple(const PlanParams& a, const PlanParams& b, const PlanParams& c, hipStream_t stream) {
-  hipLaunchKernelGGL(plan_triple_kernel, dim3(3), dim3(THREADS), 0, stream, a, b, c);
+  hipLaunchKernelGGL(plan_triple_kernel, dim3(3), dim3(THREADS), 0, stream, PlanList<3>{{a, b, c}});
   return hipGetLastError();
 }
 
