@@ -98,9 +98,10 @@ def _paired_layout(nbq: int, nbk: int) -> torch.Tensor:
     return lay
 
 
-# (head_dim, seq): 3, 63 (odd, ragged) and 64 layout rows are paired by overlap; 65 rows take
-# rows 2t and 2t + 1
-PAIRED = ((64, 150), (128, 4022), (64, 4096), (64, 4100))
+# (head_dim, seq, layout at an odd address): 3, 63 (odd, ragged) and 64 layout rows are paired by
+# overlap (64 key tiles per row: the planner builds the rows' masks while it copies the layout,
+# unless the layout is not 16-byte aligned); 65 rows take rows 2t and 2t + 1
+PAIRED = ((64, 150, False), (128, 4022, False), (64, 4096, False), (64, 4096, True), (64, 4100, False))
 
 
 @pytest.mark.parametrize("case", PAIRED, ids=lambda c: "-".join(map(str, c)))
@@ -108,15 +109,24 @@ def test_block_rows_paired_by_overlap(gpu_available, case):
     """Forward and two-pass backward under a shared block layout whose 128-row query tiles take
     the two layout rows the planner pairs by shared kept tiles (the kernels look the rows up per
     tile), against the oracle element by element, into NaN-filled outputs."""
-    d, s = case
+    d, s, odd = case
     w = _w("bf16", d, "block", 1, 2, 1, s, backward=True)
     inp = make_inputs(w, 1300 + s + d)
-    inp["layout"] = _paired_layout(-(-s // 64), -(-s // 64))
+    nb = -(-s // 64)
+    inp["layout"] = _paired_layout(nb, nb)
+    ref_mask = oracle_mask(w, inp)
+    if odd:
+        # the same layout one byte into a device buffer (a device tensor passes through the helpers'
+        # .to() and .contiguous() unchanged, storage offset included)
+        buf = torch.zeros(nb * nb + 1, dtype=torch.uint8, device="cuda")
+        buf[1:] = inp["layout"].reshape(-1).to("cuda")
+        inp["layout"] = buf[1:].view(nb, nb)
+        assert inp["layout"].data_ptr() % 16 == 1
     say(f"block rows paired by overlap {case}")
     o, lse = fwd_into_nan(w, inp)
     q, k, v = to_np64(inp["q"]), to_np64(inp["k"]), to_np64(inp["v"])
-    o_ref, lse_ref = oracle.attention_fwd(q, k, v, oracle_mask(w, inp), inp["scale"])
+    o_ref, lse_ref = oracle.attention_fwd(q, k, v, ref_mask, inp["scale"])
     compare_fwd(to_np64(o), to_np64(lse), o_ref, lse_ref, TOL_BF16_FWD, str(case))
     grads = bwd_into_nan(w, inp, o, lse)
-    ref = oracle.attention_bwd(q, k, v, to_np64(inp["do"]), oracle_mask(w, inp), inp["scale"])
+    ref = oracle.attention_bwd(q, k, v, to_np64(inp["do"]), ref_mask, inp["scale"])
     check_grads(tuple(to_np64(g) for g in grads), ref, str(case))
