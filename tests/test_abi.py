@@ -271,6 +271,30 @@ def test_single_pass_backward_arguments():
     assert call(B.ATTN_BWD_PLANNED, two - 1) == B.ATTN_ERR_WORKSPACE
 
 
+def test_row_pairing_workspace():
+    """A block layout shared by every (batch, head), of at most 64 rows and 64 key tiles, gets a
+    row-pairs region (4 bytes per 128-row query tile, 256-byte aligned) in the bf16 forward's and
+    the two-pass backward's workspaces; per-head layouts, more rows or other dtypes do not."""
+    lib = _lib()
+    layout = _spaced(1)[0]
+
+    def sizes(sq, sk, dtype=B.ATTN_BF16, per_head=False):
+        p = _problem(b=2, hq=4, hkv=2, sq=sq, sk=sk, d=128, dtype=dtype)
+        nbq, nbk = -(-sq // 64), -(-sk // 64)
+        m = _mask(kind=3, layout=layout, sb=4 * nbq * nbk if per_head else 0, sh=nbq * nbk if per_head else 0)
+        fwd = lib.attn_fwd_workspace_bytes(ctypes.byref(p), ctypes.byref(m))
+        bwd = lib.attn_bwd_workspace_bytes(ctypes.byref(p), ctypes.byref(m)) if dtype == B.ATTN_BF16 else 0
+        return fwd, bwd
+
+    for sq, sk in ((4096, 4096), (4022, 4022), (150, 4096), (4096, 300)):
+        shared, per_head = sizes(sq, sk), sizes(sq, sk, per_head=True)
+        assert shared[0] - per_head[0] == 256 and shared[1] - per_head[1] == 256, (sq, sk)
+    for sq, sk in ((4100, 4096), (4096, 4160)):   # 65 rows; 65 key tiles per row
+        assert sizes(sq, sk) == sizes(sq, sk, per_head=True), (sq, sk)
+    for dtype in (B.ATTN_F32, B.ATTN_FP8_E4M3):
+        assert sizes(4096, 4096, dtype)[0] == sizes(4096, 4096, dtype, per_head=True)[0]
+
+
 def _fwd_plan(lib, p, m, bws, bws_bytes, ptrs=None):
     ptrs = ptrs or _fwd_ok_ptrs()
     return lib.attn_fwd_with_bwd_plan(ctypes.byref(p), ptrs["q"], ptrs["k"], ptrs["v"], ctypes.byref(m), 0.125,
