@@ -3,7 +3,7 @@
 // The generic mask of the fused multi-head attention operator write-up (zwxr.cn), section 3.3,
 // is one byte per (query, key) pair: 0 sends the score to minus infinity. The attention kernels
 // cannot afford a byte load per score, and should not visit 64x64 blocks the mask hides
-// entirely (the write-up's "skip blocks that need no compute"). One pass over the byte mask
+// entirely (the write-up advises skipping blocks with no work in them). One pass over the byte mask
 // therefore produces, per distinct (batch element, query head) of the mask:
 //   * row bits: bit k % 32 of word k / 32 of query row q (the forward and the dQ pass read the
 //     32 keys of one half-tile with one word per lane);

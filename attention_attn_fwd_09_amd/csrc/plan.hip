@@ -2,13 +2,14 @@
 //
 // The report on the Xingchen-Cup sparse FlashAttention operator (smzdm.com), section 03, stresses
 // that the kept blocks of a sparse (or causal) mask are unevenly spread, so a static split leaves
-// cores idle; the fused-attention write-up (zwxr.cn), section 4.2, finds that "whoever finishes
-// first takes the next block" beats a static split. Here the items are sorted by cost, longest
-// first, and launched as one workgroup each: the hardware dispatcher hands the next item in the
-// list to whichever compute unit frees up first, which is that dynamic policy with a
+// cores idle; the fused-attention write-up (zwxr.cn), section 4.2, finds a dynamic hand-out, where
+// a core that is done fetches the next block, faster than a static split. Here the items are sorted
+// by cost, longest first, and launched as one workgroup each: the hardware dispatcher hands the next
+// item in the list to whichever compute unit frees up first, which is that dynamic policy with a
 // longest-processing-time order on top. The same report's opening anecdote (147 microseconds of an
-// idle chip spent in a clumsy statistics step) warns that a slow prologue can cost more than it saves, so this is one short kernel with one workgroup:
-// a cost histogram in LDS, a scan, and a scatter.
+// idle chip spent in a clumsy statistics step) warns that a slow prologue can cost more than it
+// saves, so this is one short kernel with one workgroup: a cost histogram in LDS, a scan, and a
+// scatter.
 //
 // Items:
 //   FWD_Q / BWD_Q: (b, h_q, q-tile of BM rows), cost = number of 64-key tiles the tile visits.
