@@ -577,22 +577,24 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdParams p) {
 
 // ------------------------------------------------------------------------------------------------
 // dK/dV pass with wave pairs (two-pass mode). One workgroup per 64-key tile, four waves: two pairs
-// of 32 keys. In a pair, the P wave computes S = Q K^T (its accumulator starts at -LSE / scale, so
-// P = exp2(scale log2(e) acc)), P, and dV += P^T dO; the dP wave computes dP - Delta = dO V^T (its
-// accumulator starts at -Delta), then dS = P (dP - Delta) with the P it receives through LDS, and
-// dK += dS^T Q. Each wave holds only K or V fragments and one accumulator, half of what a wave
-// doing all four products needs, so two waves share each SIMD and cover each other's latencies.
-// No product is computed twice; P crosses once per step, as bf16 (4 KiB per pair).
-// A step is one 64-row query tile of one query head of the group: copy barrier, P-wave scores and
-// exponentials (dP-wave scores alongside), exchange barrier, then the two gradient products.
+// of 32 keys. A step is one 64-row query tile of one query head of the group, two blocks of 32
+// queries. Wave r of a pair owns query block r of every step: it computes S = Q K^T (accumulator
+// seeded with -LSE / scale, so P = exp2(scale log2(e) acc)) and dP - Delta = dO V^T (seeded with
+// -Delta) for its block, then P and dS = P (dP - Delta). Wave 0 accumulates dV += P^T dO, wave 1
+// dK += dS^T Q: each adds its own block at once and, after one exchange barrier, the partner's,
+// which the partner hands over in bf16 through LDS (dS of block 0 to wave 1, P of block 1 to
+// wave 0; 4 KiB per pair). Each wave holds K and V fragments and one accumulator, so two waves
+// share each SIMD and cover each other's latencies; no product is computed twice, and each wave
+// runs half of the step's exponentials. A step: copy barrier, scores, exponentials, own-block
+// product, exchange barrier, partner-block product.
 constexpr int PAIR_LEAD = 4;   // k-steps of row-fragment reads in flight ahead of the score MFMAs
-constexpr int PAIR_PRIO_MIN_STEPS = 24;   // steps per item from which the P wave runs at raised priority
+constexpr int PAIR_PRIO_MIN_STEPS = 32;   // steps per item from which the hand-over runs at raised priority
 
 template <int D>
 struct PairLds {
   static constexpr int TILE = BQ * D * 2;
   static constexpr int STATS = 256;          // 64 row values
-  static constexpr int XCH = 4096;           // one pair's P: [query block][half][lane] x 16 bytes
+  static constexpr int XCH = 4096;           // one pair's hand-over: [dS0 | P1][half][lane] x 16 bytes
   static constexpr int MAX_STEPS = 2048;     // listed (query head, layout row) pairs for block masks
 };
 
@@ -627,9 +629,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MINW))) voi
 
   // Pair and role of this wave. A CU holds two of these workgroups (workgroup slots 0 and 1), and
   // the four waves of each spread over the four SIMDs. Ranking the waves by SIMD and flipping the
-  // role with the slot's parity puts one P wave and one dP wave on every SIMD, so the exponentials
-  // of one run under the MFMAs of the other. Any placement gives a valid assignment: the ranks are
-  // a permutation, and each pair gets one wave of each role.
+  // role with the slot's parity puts one wave of each role on every SIMD. Any placement gives a
+  // valid assignment: the ranks are a permutation, and each pair gets one wave of each role.
   const uint32_t hw_id = __builtin_amdgcn_s_getreg((31 << 11) | 4);   // HW_REG_HW_ID
   const int my_simd = (int)((hw_id >> 4) & 3), slot = (int)((hw_id >> 16) & 1);
   if (lane == 0) simd_of[wave] = my_simd;
@@ -641,7 +642,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MINW))) voi
     rank += (sw < my_simd || (sw == my_simd && w < wave)) ? 1 : 0;
   }
   rank = __builtin_amdgcn_readfirstlane(rank);
-  const int pair = rank >> 1, role = (rank & 1) ^ slot;   // role 0: S, P, dV; role 1: dP, dS, dK
+  const int pair = rank >> 1, role = (rank & 1) ^ slot;   // role r: query block r, then dV (0) or dK (1)
 
   const uint32_t item = p.items_kv[blockIdx.x];
   // an item outside the problem (a list the caller kept from another call) does nothing
@@ -654,14 +655,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MINW))) voi
   const int my_k = kp0 + c;
 
   const size_t kv_off = ((size_t)(b * p.heads_kv + kvh) * p.seq_k) * D;
-  // K rows (P wave) or V rows (dP wave) of this lane's key: B operand of S = Q K^T or dP = dO V^T
-  const __amdgpu_buffer_rsrc_t rf =
-      make_rsrc((const bf16*)(role == 0 ? p.k : p.v) + kv_off, (uint32_t)p.seq_k * RB);
-  bf16x8 frag[KS];
+  // K and V rows of this lane's key: B operands of S = Q K^T and dP = dO V^T
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const bf16*)p.k + kv_off, (uint32_t)p.seq_k * RB);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const bf16*)p.v + kv_off, (uint32_t)p.seq_k * RB);
+  bf16x8 kfrag[KS], vfrag[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-    frag[ks] = __builtin_bit_cast(
-        bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rf, (uint32_t)my_k * RB + (uint32_t)(ks * 32 + hh * 16), 0, 0));
+  for (int ks = 0; ks < KS; ++ks) {
+    const uint32_t off = (uint32_t)my_k * RB + (uint32_t)(ks * 32 + hh * 16);
+    kfrag[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+    vfrag[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
+  }
 
   // ---- the (query head, query tile) steps that see this key tile ----
   int kv_len = p.seq_k, q_len = p.seq_q;
@@ -767,17 +770,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MINW))) voi
   // this pair's P exchange tile; lane-linear 16-byte chunks, so writes and reads are conflict free
   char* xp = xch + pair * L::XCH + lane * 16;
 
-  // dense mask: bits of the step's queries q0 .. q0+63 for this lane's key and the step's query
-  // head (0 past the key range), two words; loaded one step ahead of the step that tests them
-  auto dcol_words = [&](int s, uint32_t (&w)[2]) __attribute__((always_inline)) {
+  // dense mask: bits of the queries q0 + qoff .. q0 + qoff + 31 of step s (this wave's query block)
+  // for this lane's key and the step's query head (0 past the key range), in w[0]; loaded one step
+  // ahead of the step that tests them
+  auto dcol_words = [&](int s, int qoff, uint32_t (&w)[2]) __attribute__((always_inline)) {
     int g, qt;
     step_at(s, g, qt);
     const uint32_t* dcol = p.dense.cols + b * p.dense.cols_stride_b + (kvh * p.group + g) * p.dense.cols_stride_h +
                            (int64_t)min(my_k, p.seq_k - 1) * p.dense.col_words;
-    dense_words(dcol, my_k < p.seq_k, p.dense.col_words, qt * BQ, w);
+    dense_words(dcol, my_k < p.seq_k, p.dense.col_words, qt * BQ + qoff, w);
   };
 
-  f32x16 acc[DB];   // dV (P wave) or dK / scale (dP wave) of this pair's 32 keys
+  f32x16 acc[DB];   // dV (role 0) or dK / scale (role 1) of this pair's 32 keys
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
   const float cs = p.scale_log2;
@@ -793,22 +797,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MINW))) voi
     }
     return r;
   };
-  // the two 32-query blocks' accumulators seeded from `st`, then += rows(tile) x frag^T (two
-  // interleaved MFMA chains). The row-fragment reads run PAIR_LEAD k-steps ahead of the MFMAs that
-  // consume them (order pinned with sched_group_barrier; masks 0x100 LDS read, 0x008 MFMA).
-  auto scores = [&](const char* tile, const char* st, f32x16 (&a)[2]) __attribute__((always_inline)) {
-    a[0] = stats16(st, 0);
-    a[1] = stats16(st, 1);
-    bf16x8 x0[KS], x1[KS];
+  // S (seeded with -LSE / scale) and dP - Delta (seeded with -Delta) of query block QB, as two
+  // interleaved MFMA chains over the Q and dO rows of the block. The row-fragment reads run
+  // PAIR_LEAD k-steps ahead of the MFMAs that consume them (order pinned with
+  // sched_group_barrier; masks 0x100 LDS read, 0x008 MFMA).
+  auto scores = [&](auto qb_tag, const char* qtile, const char* otile, const char* sst, const char* dst, f32x16& sa,
+                    f32x16& da) __attribute__((always_inline)) {
+    constexpr int QB = decltype(qb_tag)::value;
+    sa = stats16(sst, QB);
+    da = stats16(dst, QB);
+    bf16x8 xq[KS], xo[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      x0[ks] = *(const bf16x8*)(tile + roff[ks]);
-      x1[ks] = *(const bf16x8*)(tile + roff[ks] + 32 * RB);
+      xq[ks] = *(const bf16x8*)(qtile + roff[ks] + QB * 32 * RB);
+      xo[ks] = *(const bf16x8*)(otile + roff[ks] + QB * 32 * RB);
     }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      a[0] = mfma32(x0[ks], frag[ks], a[0]);
-      a[1] = mfma32(x1[ks], frag[ks], a[1]);
+      sa = mfma32(xq[ks], kfrag[ks], sa);
+      da = mfma32(xo[ks], vfrag[ks], da);
     }
     constexpr int KL = PAIR_LEAD < KS ? PAIR_LEAD : KS;
     __builtin_amdgcn_sched_group_barrier(0x100, 8 + 2 * KL, 0);   // the 8 seed reads, KL k-steps
@@ -845,7 +852,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MINW))) voi
 
   uint32_t dcur[2] = {0u, 0u}, dnext[2] = {0u, 0u};
 
-  // One step of the P wave (ROLE 0) or the dP wave (ROLE 1). Every wave passes both barriers of
+  // One step of wave ROLE of a pair. Every wave passes both barriers of
   // every step; a pair whose keys see none of the step's queries skips its products.
   auto step = [&](auto role_tag, auto stage_tag, auto masked_tag, int s) __attribute__((always_inline)) {
     constexpr int ROLE = decltype(role_tag)::value;
@@ -859,10 +866,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MINW))) voi
     int g, qt;
     step_at(s, g, qt);
     const int q0 = qt * BQ;
-    if constexpr (ROLE == 0 && MASK == MASK_DENSE) {
+    if constexpr (MASK == MASK_DENSE) {
       dcur[0] = dnext[0];
-      dcur[1] = dnext[1];
-      if (s + 1 < n_steps) dcol_words(s + 1, dnext);
+      if (s + 1 < n_steps) dcol_words(s + 1, ROLE * 32, dnext);
     }
     bool active = true;
     if constexpr (MASKED) {
@@ -870,78 +876,53 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MINW))) voi
       if constexpr (MASK == MASK_CAUSAL) active = active && kp0 <= q0 + BQ - 1;
       if constexpr (MASK == MASK_PADDING) active = active && q0 < q_len;
     }
-    // P crosses one 32-query block at a time (one barrier per block), so that the P wave's
-    // exponentials of block 1 run under its own dV products of block 0 and the dP wave starts on
-    // block 0 half a step earlier.
-    bf16x8 t0[2][DB], t1[2][DB];   // transposed fragments of the two query blocks
-    if constexpr (ROLE == 0) {
-      // the P wave's scores and exponentials gate its partner: on long items they go first at the
-      // instruction arbiter (on items of a few steps this measured slower, so they do not)
+    // Wave ROLE owns query block QB = ROLE of the step: its S, P, dP - Delta and dS. It adds its
+    // own block's product to its accumulator (dV += P0^T dO0 for ROLE 0, dK += dS1^T Q1 for
+    // ROLE 1), hands its partner the operand the partner accumulates (dS0 to ROLE 1, P1 to
+    // ROLE 0) through LDS, and after one barrier adds the partner's block.
+    constexpr int QB = ROLE;
+    const char* tt = ROLE == 0 ? dol : ql;   // transposed operand: dO (dV) or Q (dK)
+    bf16x8 t_own[2][DB], t_other[2][DB];
+    if (active) {
+      // what the partner waits for goes first at the instruction arbiter on long items (on items
+      // of a few steps this measured slower, so they do not)
       if (n_steps >= PAIR_PRIO_MIN_STEPS) __builtin_amdgcn_s_setprio(2);
-      f32x16 sc[2];
-      if (active) {
-        scores(ql, ST == 0 ? s_st0 : s_st1, sc);
-        load_t(dol, 0, t0);
-      }
+      f32x16 sc, dp;
+      scores(std::integral_constant<int, QB>{}, ql, dol, ST == 0 ? s_st0 : s_st1, ST == 0 ? d_st0 : d_st1, sc, dp);
+      load_t(tt, QB, t_own);
+      float pv[16], ds[16];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        bf16x8 pb[2];
-        if (active) {
-          float pv[16];
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            pv[i] = fast_exp2(sc[qb][i] * cs);
-            if constexpr (MASKED) {
-              const int q = q0 + qb * 32 + hh * 16 + i;
-              bool vis = q < q_len && my_k < kv_len;
-              if constexpr (MASK == MASK_CAUSAL) vis = vis && my_k <= q;
-              if constexpr (MASK == MASK_DENSE) vis = vis && ((dcur[qb] >> (hh * 16 + i)) & 1u);
-              pv[i] = vis ? pv[i] : 0.0f;
-            }
-          }
-          pb[0] = pack_bf16x8(pv);
-          pb[1] = pack_bf16x8(pv + 8);
-          *(bf16x8*)(xp + qb * 2048) = pb[0];
-          *(bf16x8*)(xp + qb * 2048 + 1024) = pb[1];
+      for (int i = 0; i < 16; ++i) {
+        pv[i] = fast_exp2(sc[i] * cs);
+        if constexpr (MASKED) {
+          const int q = q0 + QB * 32 + hh * 16 + i;
+          bool vis = q < q_len && my_k < kv_len;
+          if constexpr (MASK == MASK_CAUSAL) vis = vis && my_k <= q;
+          if constexpr (MASK == MASK_DENSE) vis = vis && ((dcur[0] >> (hh * 16 + i)) & 1u);
+          pv[i] = vis ? pv[i] : 0.0f;
         }
-        if (qb == 1) __builtin_amdgcn_s_setprio(0);
-        lds_barrier();   // P of block qb is in LDS for the dP wave
-        if (active) {
-          if (qb == 0) {
-            load_t(dol, 1, t1);
-            grads(pb, t0);   // dV += P^T dO
-          } else {
-            grads(pb, t1);
-          }
-        }
+        ds[i] = pv[i] * dp[i];
       }
-    } else {
-      f32x16 dp[2];
-      if (active) {
-        scores(dol, ST == 0 ? d_st0 : d_st1, dp);   // dP - Delta
-        load_t(ql, 0, t0);
+      const bf16x8 pb[2] = {pack_bf16x8(pv), pack_bf16x8(pv + 8)};
+      const bf16x8 db[2] = {pack_bf16x8(ds), pack_bf16x8(ds + 8)};
+      if constexpr (ROLE == 0) {
+        *(bf16x8*)(xp) = db[0];
+        *(bf16x8*)(xp + 1024) = db[1];
+        __builtin_amdgcn_s_setprio(0);
+        grads(pb, t_own);   // dV += P0^T dO0
+      } else {
+        *(bf16x8*)(xp + 2048) = pb[0];
+        *(bf16x8*)(xp + 3072) = pb[1];
+        __builtin_amdgcn_s_setprio(0);
+        grads(db, t_own);   // dK += dS1^T Q1
       }
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        lds_barrier();
-        if (active) {
-          const bf16x8 p0 = *(const bf16x8*)(xp + qb * 2048);
-          const bf16x8 p1 = *(const bf16x8*)(xp + qb * 2048 + 1024);
-          float ds[16];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            ds[i] = (float)p0[i] * dp[qb][i];
-            ds[8 + i] = (float)p1[i] * dp[qb][8 + i];
-          }
-          const bf16x8 dsb[2] = {pack_bf16x8(ds), pack_bf16x8(ds + 8)};
-          if (qb == 0) {
-            load_t(ql, 1, t1);
-            grads(dsb, t0);   // dK += dS^T Q
-          } else {
-            grads(dsb, t1);
-          }
-        }
-      }
+      load_t(tt, 1 - QB, t_other);
+    }
+    lds_barrier();   // the partner's operand is in LDS
+    if (active) {
+      const char* src = xp + (1 - ROLE) * 2048;
+      const bf16x8 got[2] = {*(const bf16x8*)src, *(const bf16x8*)(src + 1024)};
+      grads(got, t_other);   // dV += P1^T dO1 (ROLE 0) or dK += dS0^T Q0 (ROLE 1)
     }
   };
   auto run_role = [&](auto role_tag) __attribute__((always_inline)) {
@@ -959,12 +940,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MINW))) voi
   };
 
   if constexpr (MASK == MASK_DENSE)
-    if (role == 0 && n_steps > 0) dcol_words(0, dnext);
+    if (n_steps > 0) dcol_words(0, role * 32, dnext);
   if (n_steps > 0) issue_step(std::integral_constant<int, 0>{}, 0);
   if (role == 0) run_role(std::integral_constant<int, 0>{});
   else run_role(std::integral_constant<int, 1>{});
 
-  // ---- write dV (P wave) or dK = scale * acc (dP wave); lane (c, hh) holds column db*32 + c of
+  // ---- write dV (role 0) or dK = scale * acc (role 1); lane (c, hh) holds column db*32 + c of
   // keys kp0 + (i / 4) * 8 + hh * 4 + i % 4 ----
   bf16* out = (bf16*)(role == 0 ? p.dv : p.dk) + kv_off;
   const float f = role == 0 ? 1.0f : p.scale;
