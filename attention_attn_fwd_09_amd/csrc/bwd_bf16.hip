@@ -767,7 +767,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MINW))) voi
       toff[db][half] = row * RB + (((d >> 3) ^ swz<D>(row)) * 16) + (d & 7) * 2;
     }
   }
-  // this pair's P exchange tile; lane-linear 16-byte chunks, so writes and reads are conflict free
+  // this pair's hand-over tile (dS of block 0 at +0, P of block 1 at +2048); lane-linear 16-byte
+  // chunks, so writes and reads are conflict free
   char* xp = xch + pair * L::XCH + lane * 16;
 
   // dense mask: bits of the queries q0 + qoff .. q0 + qoff + 31 of step s (this wave's query block)
