@@ -947,16 +947,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MINW))) voi
   else run_role(std::integral_constant<int, 1>{});
 
   // ---- write dV (role 0) or dK = scale * acc (role 1); lane (c, hh) holds column db*32 + c of
-  // keys kp0 + (i / 4) * 8 + hh * 4 + i % 4 ----
+  // keys kp0 + (i / 4) * 8 + hh * 4 + i % 4. Each wave stages its 32 rows in bf16 through LDS (the
+  // Q/dO stage buffers, free once every wave has passed the last step) and writes whole rows with
+  // 16-byte stores. ----
   bf16* out = (bf16*)(role == 0 ? p.dv : p.dk) + kv_off;
   const float f = role == 0 ? 1.0f : p.scale;
+  __syncthreads();   // every wave is done with the last step's tiles
+  char* rows_lds = (wave < 2 ? q_st0 : q_st1) + (wave & 1) * (32 * RB);
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int key = kp0 + (i >> 2) * 8 + hh * 4 + (i & 3);
-      if (key < p.seq_k) out[(size_t)key * D + db * 32 + c] = (bf16)(acc[db][i] * f);
+      const int r = (i >> 2) * 8 + hh * 4 + (i & 3);
+      *(bf16*)(rows_lds + r * RB + (db * 32 + c) * 2) = (bf16)(acc[db][i] * f);
     }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the wave's own rows are in LDS
+  constexpr int CPR = RB / 16;                          // 16-byte chunks per row
+#pragma unroll
+  for (int j = 0; j < 32 * CPR / 64; ++j) {
+    const int chunk = j * 64 + lane;
+    const int r = chunk / CPR, cc = chunk % CPR;
+    const uint4 v = *(const uint4*)(rows_lds + r * RB + cc * 16);
+    if (kp0 + r < p.seq_k) *(uint4*)(out + (size_t)(kp0 + r) * D + cc * 8) = v;
   }
 }
 
