@@ -1252,19 +1252,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
   run(std::false_type{}, 0, n_free);
   run(std::true_type{}, n_free, n_tiles);
 
-  if (my_q < p.seq_q) {
-    bf16* dqg = (bf16*)p.dq + q_off + (size_t)my_q * D;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        bf16x4 v4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v4[e] = (bf16)(acc[db][g4 * 4 + e] * p.scale);
-        *(bf16x4*)(dqg + db * 32 + g4 * 8 + hh * 4) = v4;
-      }
-    }
-  }
+  // dQ as whole rows, staged in one of the four K/V stage arrays per wave (free once every wave has
+  // passed the last tile)
+  static_assert(NW <= 4 && 32 * (RB + 16) <= L::TILE, "one stage array per wave");
+  __syncthreads();
+  char* rows_lds = wave == 0 ? k_st0 : wave == 1 ? v_st0 : wave == 2 ? k_st1 : v_st1;
+  write_rows_bf16<D>(rows_lds, acc, p.scale, lane, (bf16*)p.dq + q_off + (size_t)qw0 * D, p.seq_q - qw0);
 }
 
 // ------------------------------------------------------------------------------------------------

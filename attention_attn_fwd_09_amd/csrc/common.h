@@ -206,4 +206,36 @@ __device__ __forceinline__ void dense_words(const uint32_t* row_bits, bool row_o
   w[1] = (row_ok && w0 + 1 < row_words) ? row_bits[w0 + 1] : 0u;
 }
 
+
+// Writes a wave's 32 output rows of D bf16 columns, held in the MFMA accumulator layout of O^T and
+// dQ^T (lane (c, hh) holds row c, columns db*32 + g4*8 + hh*4 + 0..3 in acc[db][g4*4 + 0..3]),
+// scaled by the lane's factor f, as whole rows: the rows go to `lds` (32 rows of 2D + 16 bytes; the
+// padding puts the 32 rows of one write on distinct banks) and come back as 16-byte chunks, one
+// store each. Rows at or past `rows` are not written. `lds` holds 32 * (2D + 16) bytes that no
+// other wave touches meanwhile.
+template <int D>
+__device__ __forceinline__ void write_rows_bf16(char* lds, const f32x16 (&acc)[D / 32], float f, int lane, bf16* out,
+                                                int rows) {
+  constexpr int DB = D / 32, RBP = 2 * D + 16, CPR = 2 * D / 16;
+  const int c = lane & 31, hh = lane >> 5;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      bf16x4 v4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v4[e] = (bf16)(acc[db][g4 * 4 + e] * f);
+      *(bf16x4*)(lds + c * RBP + (db * 32 + g4 * 8 + hh * 4) * 2) = v4;
+    }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the wave's rows are in LDS
+#pragma unroll
+  for (int j = 0; j < 32 * CPR / 64; ++j) {
+    const int chunk = j * 64 + lane;
+    const int r = chunk / CPR, cc = chunk % CPR;
+    const uint4 v = *(const uint4*)(lds + r * RBP + cc * 16);
+    if (r < rows) *(uint4*)(out + (size_t)r * D + cc * 8) = v;
+  }
+}
+
 }  // namespace attn

@@ -351,22 +351,33 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
     }
     return;
   }
-  if (my_q < p.seq_q) {
-    bf16* og = (bf16*)p.o + q_off + (size_t)my_q * D;
+  // Under the listed and padding masks O goes out as whole rows through LDS (2-4% faster there);
+  // the no-mask and causal kernels store each lane's 8-byte pieces directly (as fast or faster)
+  if constexpr (MASK == MASK_NONE || MASK == MASK_CAUSAL) {
+    if (my_q < p.seq_q) {
+      bf16* og = (bf16*)p.o + q_off + (size_t)my_q * D;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+      for (int db = 0; db < DB; ++db) {
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        bf16x4 v4;
+        for (int g4 = 0; g4 < 4; ++g4) {
+          bf16x4 v4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v4[e] = (bf16)(acc[db][g4 * 4 + e] * inv);
-        *(bf16x4*)(og + db * 32 + g4 * 8 + hh * 4) = v4;
+          for (int e = 0; e < 4; ++e) v4[e] = (bf16)(acc[db][g4 * 4 + e] * inv);
+          *(bf16x4*)(og + db * 32 + g4 * 8 + hh * 4) = v4;
+        }
       }
     }
-    if (hh == 0) {
-      const float lse = empty ? -INFINITY : (m_run + __builtin_amdgcn_logf(l)) * 0.69314718055994530942f;
-      p.lse[(size_t)(b * p.heads_q + h) * p.seq_q + my_q] = lse;
-    }
+  } else {
+    // O as whole rows, staged in one of the four K/V stage arrays per wave (free once every wave
+    // has passed the last tile)
+    static_assert(NW <= 4 && 32 * (RB + 16) <= L::TILE_BYTES, "one stage array per wave");
+    __syncthreads();
+    char* rows_lds = wave == 0 ? k_st0 : wave == 1 ? v_st0 : wave == 2 ? k_st1 : v_st1;
+    write_rows_bf16<D>(rows_lds, acc, inv, lane, (bf16*)p.o + q_off + (size_t)qw0 * D, p.seq_q - qw0);
+  }
+  if (my_q < p.seq_q && hh == 0) {
+    const float lse = empty ? -INFINITY : (m_run + __builtin_amdgcn_logf(l)) * 0.69314718055994530942f;
+    p.lse[(size_t)(b * p.heads_q + h) * p.seq_q + my_q] = lse;
   }
 }
 
