@@ -370,7 +370,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MINW)))
   } else {
     // O as whole rows, staged in one of the four K/V stage arrays per wave (free once every wave
     // has passed the last tile)
-    static_assert(NW <= 4 && 32 * (RB + 16) <= L::TILE_BYTES, "one stage array per wave");
+    static_assert(NW <= 4 && 32 * (RB + 8) <= L::TILE_BYTES, "one stage array per wave");
     __syncthreads();
     char* rows_lds = wave == 0 ? k_st0 : wave == 1 ? v_st0 : wave == 2 ? k_st1 : v_st1;
     write_rows_bf16<D>(rows_lds, acc, inv, lane, (bf16*)p.o + q_off + (size_t)qw0 * D, p.seq_q - qw0);
