@@ -255,8 +255,9 @@ struct BwdSizes {
   DenseSizes dense;
 };
 
-// Two-pass layout: -Delta, LSE*log2(e), dK/dV items, dQ items. Single pass (ATTN_BWD_ATOMIC_DQ):
-// -Delta, LSE*log2(e), dK/dV items, then the fp32 dQ accumulator [B, Hq, Sq, D].
+// Two-pass layout: -Delta, LSE*log2(e), -LSE/scale (wave-pair dK/dV kernel only), dK/dV items, dQ
+// items, the dQ list's row pairs (when paired). Single pass (ATTN_BWD_ATOMIC_DQ): -Delta, LSE*log2(e),
+// dK/dV items, then the fp32 dQ accumulator [B, Hq, Sq, D]. A dense mask's packed bits follow either.
 BwdSizes bwd_sizes(const attn_problem* p, const attn_mask* m, int32_t flags = 0) {
   BwdSizes s;
   s.dkdv = bwd_dkdv_variant(m->kind, flags, p->heads_q / p->heads_kv, ceil_div(p->seq_q, 64));

@@ -196,9 +196,9 @@ __device__ __forceinline__ void split_item(uint32_t w, int n_items, int kv_split
 __device__ __forceinline__ int clamp_len(int32_t len, int seq) { return len < 0 ? 0 : (len > seq ? seq : len); }
 
 // A dense mask's bits of one row (or column) for the 64 positions k0 .. k0+63: two 32-bit words,
-// 0 past the row's words or for a row past the sequence. The dK/dV pass, which runs one wave per
-// SIMD, loads them one step ahead of the step that tests them, so that the load's latency is spent
-// under the previous step's work (the kernels with two waves per SIMD hide it without that).
+// 0 past the row's words or for a row past the sequence. The dK/dV kernels load them one step
+// ahead of the step that tests them, so that the load's latency is spent under the previous step's
+// work; the forward and the dQ pass load them in the step that uses them.
 __device__ __forceinline__ void dense_words(const uint32_t* row_bits, bool row_ok, int row_words, int k0,
                                             uint32_t (&w)[2]) {
   const int w0 = k0 >> 5;
